@@ -1,0 +1,206 @@
+"""Python binding of libmoe_w4a16.so, the MI355X (gfx950) fused W4A16 MoE layer.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. Functions carry the C names of include/moe_w4a16.h and take torch
+tensors (device memory) or raw integer device pointers; torch supplies memory
+and the current HIP stream. If the library has not been built this module
+raises on import -- there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+
+MOE_FMT_NVFP4_E4M3_K16 = 1
+MOE_FMT_MXFP4_E8M0_K32 = 2
+MOE_ACT_SILU_SWIGLU = 1
+MOE_ACT_RELU2 = 2
+MOE_DECODE_MAX_M = 16
+
+FMT = {"nvfp4": MOE_FMT_NVFP4_E4M3_K16, "mxfp4": MOE_FMT_MXFP4_E8M0_K32}
+ACT = {"silu_swiglu": MOE_ACT_SILU_SWIGLU, "relu2": MOE_ACT_RELU2}
+PATH = {"auto": 0, "decode": 1, "gemm": 2}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str, msg: str):
+        super().__init__(f"{where} failed with status {code}: {msg}")
+        self.code = code
+
+
+class moe_w4a16_dims(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("act", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32)]
+
+
+class moe_route_pack_view(ctypes.Structure):
+    _fields_ = [("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
+                ("sorted_route_ids", ctypes.c_void_p), ("block_expert", ctypes.c_void_p),
+                ("live", ctypes.c_void_p), ("route_slot", ctypes.c_void_p),
+                ("token_capacity", ctypes.c_int64), ("cap_routes", ctypes.c_int64),
+                ("cap_blocks", ctypes.c_int64), ("block_m", ctypes.c_int32), ("num_experts", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                          "(hipcc, gfx950). There is no CPU fallback.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    PSZ = ctypes.POINTER(ctypes.c_size_t)
+    PD = ctypes.POINTER(moe_w4a16_dims)
+    sig = {
+        "moe_route_pack_token_capacity": (I64, [I64]),
+        "moe_route_pack_workspace_size": (I32, [I64, I32, I32, I32, PSZ]),
+        "moe_route_pack": (I32, [P, I64, I32, P, I32, I32, I32, I64, P, SZ, ctypes.POINTER(moe_route_pack_view), P]),
+        "moe_w4a16_prepared_size": (I32, [PD, PSZ]),
+        "moe_w4a16_prepare": (I32, [PD, P, P, P, P, P, P, P, SZ, P]),
+        "moe_w4a16_workspace_size": (I32, [PD, I64, I32, PSZ]),
+        "moe_w4a16_fused": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_w4a16_set_path": (I32, [I32]),
+        "moe_w4a16_set_decode_max_m": (I32, [I32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = ("moe_route_pack_token_capacity", "moe_route_pack_workspace_size", "moe_route_pack",
+            "moe_w4a16_prepared_size", "moe_w4a16_prepare", "moe_w4a16_workspace_size", "moe_w4a16_fused",
+            "moe_last_error", "moe_w4a16_set_path", "moe_w4a16_set_decode_max_m")
+
+
+def lib():
+    return _lib
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    return int(t.data_ptr())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check(rc: int, where: str) -> int:
+    if rc < 0:
+        raise MoeError(rc, where, moe_last_error())
+    return rc
+
+
+def make_dims(fmt, act, num_experts: int, hidden: int, inter: int) -> moe_w4a16_dims:
+    f = FMT.get(fmt, fmt)
+    a = ACT.get(act, act)
+    return moe_w4a16_dims(int(f), int(a), int(num_experts), int(hidden), int(inter))
+
+
+def moe_last_error() -> str:
+    s = _lib.moe_last_error()
+    return s.decode() if s else ""
+
+
+def moe_route_pack_token_capacity(m: int) -> int:
+    return int(_lib.moe_route_pack_token_capacity(int(m)))
+
+
+def moe_route_pack_workspace_size(token_capacity: int, topk: int, num_local_experts: int, block_m: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.moe_route_pack_workspace_size(token_capacity, topk, num_local_experts, block_m, ctypes.byref(n)),
+           "moe_route_pack_workspace_size")
+    return n.value
+
+
+def moe_route_pack(topk_ids, m: int, topk: int, expert_map, num_global_experts: int, num_local_experts: int,
+                   block_m: int, token_capacity: int, workspace, workspace_bytes: int, stream=None) -> moe_route_pack_view:
+    view = moe_route_pack_view()
+    _check(_lib.moe_route_pack(_ptr(topk_ids), m, topk, _ptr(expert_map), num_global_experts, num_local_experts,
+                               block_m, token_capacity, _ptr(workspace), workspace_bytes, ctypes.byref(view),
+                               _stream(stream)), "moe_route_pack")
+    return view
+
+
+def moe_w4a16_prepared_size(dims: moe_w4a16_dims) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.moe_w4a16_prepared_size(ctypes.byref(dims), ctypes.byref(n)), "moe_w4a16_prepared_size")
+    return n.value
+
+
+def moe_w4a16_prepare(dims: moe_w4a16_dims, w13, s13, g13, w2, s2, g2, prepared, prepared_bytes: int,
+                      stream=None) -> None:
+    _check(_lib.moe_w4a16_prepare(ctypes.byref(dims), _ptr(w13), _ptr(s13), _ptr(g13), _ptr(w2), _ptr(s2),
+                                  _ptr(g2), _ptr(prepared), prepared_bytes, _stream(stream)), "moe_w4a16_prepare")
+
+
+def moe_w4a16_workspace_size(dims: moe_w4a16_dims, token_capacity: int, topk: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib.moe_w4a16_workspace_size(ctypes.byref(dims), token_capacity, topk, ctypes.byref(n)),
+           "moe_w4a16_workspace_size")
+    return n.value
+
+
+def moe_w4a16_fused(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: int, topk_ids, topk_weights,
+                    topk: int, expert_map, num_global_experts: int, token_capacity: int, workspace,
+                    workspace_bytes: int, out, stream=None) -> None:
+    _check(_lib.moe_w4a16_fused(ctypes.byref(dims), _ptr(prepared), prepared_bytes, _ptr(x), m, _ptr(topk_ids),
+                                _ptr(topk_weights), topk, _ptr(expert_map), num_global_experts, token_capacity,
+                                _ptr(workspace), workspace_bytes, _ptr(out), _stream(stream)), "moe_w4a16_fused")
+
+
+def moe_w4a16_set_path(path) -> int:
+    return _check(_lib.moe_w4a16_set_path(PATH.get(path, path)), "moe_w4a16_set_path")
+
+
+def moe_w4a16_set_decode_max_m(max_m: int) -> int:
+    return _check(_lib.moe_w4a16_set_decode_max_m(int(max_m)), "moe_w4a16_set_decode_max_m")
+
+
+class MoeLayer:
+    """Owns the prepared weights and a workspace for one layer shape (torch device memory)."""
+
+    def __init__(self, fmt, act, num_experts, hidden, inter, topk, token_capacity, device="cuda"):
+        import torch
+        self.dims = make_dims(fmt, act, num_experts, hidden, inter)
+        self.topk = int(topk)
+        self.token_capacity = int(token_capacity)
+        self.prepared_bytes = moe_w4a16_prepared_size(self.dims)
+        self.workspace_bytes = moe_w4a16_workspace_size(self.dims, self.token_capacity, self.topk)
+        # 256-byte alignment: torch's caching allocator hands out 512-byte aligned blocks.
+        self.prepared = torch.empty(self.prepared_bytes, dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=device)
+
+    def prepare(self, w13, s13, g13, w2, s2, g2, stream=None):
+        moe_w4a16_prepare(self.dims, w13, s13, g13, w2, s2, g2, self.prepared, self.prepared_bytes, stream)
+
+    def __call__(self, x, topk_ids, topk_weights, expert_map=None, num_global_experts=None, out=None, stream=None):
+        import torch
+        m = int(x.shape[0])
+        if out is None:
+            out = torch.empty((m, self.dims.hidden), dtype=torch.bfloat16, device=x.device)
+        ng = num_global_experts if num_global_experts is not None else (
+            int(expert_map.numel()) if expert_map is not None else self.dims.num_experts)
+        moe_w4a16_fused(self.dims, self.prepared, self.prepared_bytes, x, m, topk_ids, topk_weights, self.topk,
+                        expert_map, ng, self.token_capacity, self.workspace, self.workspace_bytes, out, stream)
+        return out

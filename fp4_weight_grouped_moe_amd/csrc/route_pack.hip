@@ -1,0 +1,195 @@
+// Route packing on gfx950: group token x expert routes by local expert into a padded,
+// power-of-two-capacity workspace (FlashInfer PR 4255, Description: shape-stable route
+// packing; Tests: expert_map and invalid expert ids). One 1024-thread workgroup does the
+// whole pack; every other workgroup of the same launch clears the fp32 output
+// accumulator of the grouped-GEMM path so that no separate launch is needed.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+#include "layout.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kPackThreads = 1024;
+constexpr int kPackWaves = kPackThreads / 64;
+
+__device__ __forceinline__ int local_expert(const RoutePackParams& p, int64_t r) {
+  if (r >= p.num_routes) return -1;
+  int g = p.topk_ids[r];
+  if (g < 0 || g >= p.num_global_experts) return -1;
+  int l = p.expert_map ? p.expert_map[g] : g;
+  return (l >= 0 && l < p.num_experts) ? l : -1;
+}
+
+// Exclusive scan of one int per thread over the 1024-thread workgroup.
+__device__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wave_tot[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    int t = lane < kPackWaves ? wave_tot[lane] : 0;
+    int s = t;
+#pragma unroll
+    for (int d = 1; d < kPackWaves; d <<= 1) {
+      int y = __shfl_up(s, d, 64);
+      if (lane >= d) s += y;
+    }
+    if (lane < kPackWaves) wave_tot[lane] = s - t;       // exclusive wave base
+    if (lane == kPackWaves - 1) wave_tot[kPackWaves] = s;  // workgroup total
+  }
+  __syncthreads();
+  int r = x - v + wave_tot[w];
+  *total = wave_tot[kPackWaves];
+  __syncthreads();
+  return r;
+}
+
+__device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = p.num_experts, B = p.block_m;
+  int* cnt = reinterpret_cast<int*>(smem);                 // [E] counts, then running slot
+  int* wave_tot = cnt + E;                                 // [kPackWaves + 1]
+  uint8_t* wcnt = reinterpret_cast<uint8_t*>(wave_tot + 32);  // [kPackWaves][E] per-wave counts
+
+  for (int e = tid; e < E; e += kPackThreads) cnt[e] = 0;
+  if (tid == 0) wave_tot[kPackWaves + 4] = 0;
+  for (int i = tid; i < kPackWaves * E; i += kPackThreads) wcnt[i] = 0;
+  __syncthreads();
+  for (int64_t r = tid; r < p.num_routes; r += kPackThreads) {
+    int l = local_expert(p, r);
+    if (l >= 0) atomicAdd(&cnt[l], 1);
+  }
+  __syncthreads();
+
+  // Padded segment offsets and the M-tile table, two experts per pass of the scan.
+  int carry = 0, tile_carry = 0;
+  for (int base = 0; base < E; base += kPackThreads) {
+    int e = base + tid;
+    int c = e < E ? cnt[e] : 0;
+    int padded = (c + B - 1) / B * B;
+    int ntile = (padded / B + kTileBlocks - 1) / kTileBlocks;
+    int tot, ttot;
+    int off = block_exclusive_scan(padded, wave_tot, &tot) + carry;
+    int toff = block_exclusive_scan(ntile, wave_tot, &ttot) + tile_carry;
+    if (e < E) {
+      p.expert_counts[e] = c;
+      p.expert_offsets[e] = off;
+      for (int b = off / B; b < (off + padded) / B; ++b) p.block_expert[b] = e;
+      for (int s = off + c; s < off + padded; ++s) {
+        p.sorted_route_ids[s] = -1;
+        if (p.slot_info) p.slot_info[s] = make_int2(-1, 0);
+      }
+      if (p.tiles) {
+        for (int t = 0; t < ntile; ++t) {
+          int first = off / B + t * kTileBlocks;
+          int nb = min(kTileBlocks, (off + padded) / B - first);
+          p.tiles[toff + t] = make_int2(first, nb | (e << 8));
+        }
+      }
+    }
+    __syncthreads();
+    if (e < E) cnt[e] = off;                               // running slot of expert e
+    carry += tot;
+    tile_carry += ttot;
+    __syncthreads();
+  }
+  const int total_padded = carry;
+  if (tid == 0) {
+    p.expert_offsets[E] = total_padded;
+    p.live[1] = total_padded;
+    p.live[2] = total_padded / B;
+    p.live[3] = int(p.m);
+    p.live[4] = tile_carry;
+  }
+  for (int64_t s = total_padded + tid; s < p.cap_routes; s += kPackThreads) {
+    p.sorted_route_ids[s] = -1;
+    if (p.slot_info) p.slot_info[s] = make_int2(-1, 0);
+  }
+  for (int64_t b = total_padded / B + tid; b < p.cap_blocks; b += kPackThreads) p.block_expert[b] = -1;
+  for (int64_t r = p.num_routes + tid; r < p.cap_k; r += kPackThreads) p.route_slot[r] = -1;
+
+  // Stable scatter, 1024 routes per chunk: rank inside the wave by matching equal expert
+  // ids, then add the counts of lower waves of the chunk and the running slot.
+  int valid_total = 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t base = 0; base < p.num_routes; base += kPackThreads) {
+    const int64_t r = base + tid;
+    const int l = local_expert(p, r);
+    int rank = 0;
+    uint64_t todo = __ballot(l >= 0);
+    valid_total += __popcll(todo);
+    while (todo) {
+      const int leader = __ffsll((long long)todo) - 1;
+      const int ev = __builtin_amdgcn_readlane(l, leader);
+      const uint64_t same = __ballot(l == ev);
+      if (l == ev) {
+        rank = __popcll(same & lt_mask);
+        if (lane == leader) wcnt[wave * E + ev] = (uint8_t)__popcll(same);
+      }
+      todo &= ~same;
+    }
+    __syncthreads();
+    if (l >= 0) {
+      int pos = cnt[l] + rank;
+      for (int w2 = 0; w2 < wave; ++w2) pos += wcnt[w2 * E + l];
+      p.sorted_route_ids[pos] = int(r);
+      p.route_slot[r] = pos;
+      if (p.slot_info) {
+        float wt = p.topk_weights ? p.topk_weights[r] : 0.f;
+        p.slot_info[pos] = make_int2(int(r / p.topk), __float_as_int(wt));
+      }
+    } else if (r < p.num_routes) {
+      p.route_slot[r] = -1;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kPackThreads) {
+      int add = 0;
+      for (int w2 = 0; w2 < kPackWaves; ++w2) {
+        add += wcnt[w2 * E + e];
+        wcnt[w2 * E + e] = 0;
+      }
+      cnt[e] += add;
+    }
+    __syncthreads();
+  }
+  // valid_total is per wave (ballots are wave-wide); lane 0 of each wave adds its share.
+  if (lane == 0) atomicAdd(&wave_tot[kPackWaves + 4], valid_total);
+  __syncthreads();
+  if (tid == 0) p.live[0] = wave_tot[kPackWaves + 4];
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParams p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  if (blockIdx.x == 0) {
+    pack_routes(p, smem);
+    return;
+  }
+  // Clear the fp32 accumulator [acc_elems] with 16-byte stores (acc_elems % 4 == 0).
+  float4* acc = reinterpret_cast<float4*>(p.acc);
+  const int64_t n4 = p.acc_elems / 4;
+  const int64_t stride = int64_t(gridDim.x - 1) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x - 1) * blockDim.x + threadIdx.x; i < n4; i += stride)
+    acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+size_t route_pack_lds_bytes(int num_experts) {
+  return size_t(num_experts) * 4 + 32 * 4 + size_t(kPackWaves) * num_experts + 16;
+}
+
+hipError_t launch_route_pack(const RoutePackParams& p, int zero_blocks, hipStream_t stream) {
+  const size_t lds = route_pack_lds_bytes(p.num_experts);
+  hipLaunchKernelGGL(route_pack_kernel, dim3(1 + (p.acc ? zero_blocks : 0)), dim3(kPackThreads), lds, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,183 @@
+/*
+ * moe_w4a16.h -- C ABI of the MI355X (gfx950) fused W4A16 mixture-of-experts layer.
+ *
+ * What the layer computes (FlashInfer PR 4255, "feat(moe): sync SM12x W4A16 fused
+ * MoE family to b12x HEAD", Description and Performance sections): for every token t
+ * and each of its top-k routes (t, j) to expert e,
+ *     h = W13_e x_t,  a = silu(h_gate) * h_up   (SiLU-SwiGLU)  or  a = max(h, 0)^2 (relu2),
+ *     out_t += w[t, j] * (W2_e a),
+ * with bf16 activations x and 4-bit E2M1 weights dequantised on the fly from
+ *   NVFP4 (one E4M3 scale per 16 along K plus one fp32 global scale per expert and
+ *          matrix), or
+ *   MXFP4 (one E8M0 scale per 32 along K; the last group of a row holds K mod 32
+ *          elements when K is not a multiple of 32 -- the page's scale tail).
+ *
+ * Conventions for every call:
+ *   - Return 0 (MOE_OK) or a negative moe_status. No exception crosses the ABI.
+ *     moe_last_error() gives a message for the last failure on the calling thread.
+ *   - Pointers named device_* or documented as device memory are HIP device
+ *     pointers; everything else is host memory. Inputs are never modified.
+ *   - All device work is enqueued on the caller's `stream`, in order. No call
+ *     allocates device or pinned memory, synchronises the stream, or reads device
+ *     data on the host; they are safe to issue during HIP graph capture. (The page's
+ *     review found a packing entry point that silently dropped its stream argument.)
+ *   - The caller owns every buffer. Sizes come from the *_size queries; a buffer that
+ *     is too small is rejected with MOE_ERR_WORKSPACE, never grown (the b12x
+ *     PR 136 Root cause: capture failed on an un-provisioned scratch arena).
+ *   - Out-of-range expert ids are data, not errors: they are dropped on the device.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,   /* a size, pointer or enum value is out of its documented range */
+  MOE_ERR_UNSUPPORTED = -2,   /* a valid request this library does not handle (device arch, shape) */
+  MOE_ERR_WORKSPACE = -3,     /* a caller buffer is smaller than its size query */
+  MOE_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+/* Weight source formats (page: Description, the fp4_e8m0_k32 source format; NVFP4 e4m3_k16). */
+typedef enum moe_source_format {
+  MOE_FMT_NVFP4_E4M3_K16 = 1,
+  MOE_FMT_MXFP4_E8M0_K32 = 2
+} moe_source_format;
+
+/* Activations between FC1 and FC2 (page: Performance, relu2 and silu rows). */
+typedef enum moe_activation {
+  MOE_ACT_SILU_SWIGLU = 1,    /* W13 rows [0, I) are gate, [I, 2I) are up; a = silu(gate) * up */
+  MOE_ACT_RELU2 = 2           /* W1 has I rows; a = max(h, 0)^2 */
+} moe_activation;
+
+/* Shape of one MoE layer's weights. hidden (H) and inter (I) must be even
+ * (two E2M1 codes per byte along K). */
+typedef struct moe_w4a16_dims {
+  int32_t fmt;          /* moe_source_format */
+  int32_t act;          /* moe_activation */
+  int32_t num_experts;  /* E, local experts held by this device */
+  int32_t hidden;       /* H */
+  int32_t inter;        /* I */
+} moe_w4a16_dims;
+
+/* ------------------------------------------------------------------ route packing
+ * Page: Description (shape-stable route packing on a power-of-two capacity, with
+ * workspaces sized to that capacity), Tests (expert_map, invalid ids, preallocated
+ * buffers, capacity contract), Review round 1 (capacity helper; minimum-one clamps).
+ *
+ * Route r = t*k + j of token t. Its local expert is expert_map[g] (or g without a
+ * map) for g = topk_ids[t][j]; the route is dropped when g < 0, g >= num_global_experts
+ * or the local id is outside [0, E). Each expert's segment lists its routes in
+ * ascending r, padded with -1 to a multiple of block_m. With cap = token capacity:
+ *   cap_routes = max(round_up(cap*k + min(E, cap*k)*(block_m-1), block_m), block_m),
+ *   cap_blocks = cap_routes / block_m.
+ */
+
+/* next power of two of max(m, 1); -1 when m < 0. One capacity serves every m <= it. */
+int64_t moe_route_pack_token_capacity(int64_t m);
+
+/* Device arrays written by moe_route_pack, all int32, pointing into the workspace. */
+typedef struct moe_route_pack_view {
+  int32_t* expert_counts;     /* [E]            valid routes per expert */
+  int32_t* expert_offsets;    /* [E+1]          padded segment starts, multiples of block_m */
+  int32_t* sorted_route_ids;  /* [cap_routes]   route id per packed slot; -1 = padding */
+  int32_t* block_expert;      /* [cap_blocks]   expert of each block; -1 after the live blocks */
+  int32_t* live;              /* [4]            {valid routes, padded routes, live blocks, m} */
+  int32_t* route_slot;        /* [cap*k]        packed slot of each route; -1 if dropped or r >= m*k */
+  int64_t token_capacity;
+  int64_t cap_routes;
+  int64_t cap_blocks;
+  int32_t block_m;
+  int32_t num_experts;
+} moe_route_pack_view;
+
+/* Bytes of device workspace moe_route_pack needs. block_m in {16, 32, 64, 128};
+ * num_local_experts in [1, 2048]; topk in [1, 64]; token_capacity a power of two
+ * in [1, 2^24]. */
+int moe_route_pack_workspace_size(int64_t token_capacity, int topk, int num_local_experts,
+                                  int block_m, size_t* bytes);
+
+/* Pack routes. topk_ids: device int32 [m, topk] row-major; expert_map: device int32
+ * [num_global_experts] or NULL (identity); m <= token_capacity. workspace: device,
+ * >= moe_route_pack_workspace_size bytes, 256-byte aligned. On success *out (host)
+ * receives the device sub-pointers. The result depends only on the inputs, never on
+ * previous contents of the workspace. */
+int moe_route_pack(const int32_t* topk_ids, int64_t m, int topk, const int32_t* expert_map,
+                   int num_global_experts, int num_local_experts, int block_m,
+                   int64_t token_capacity, void* workspace, size_t workspace_bytes,
+                   moe_route_pack_view* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------ weight preparation
+ * Page: Tests (weight preparation is bit-identical across source formats and
+ * activations), Walkthrough (layout normalisation, scale packing, W13 rotation).
+ *
+ * Canonical source layout (device memory, row-major, K fastest):
+ *   w13 u8 [E, N1, H/2]  E2M1 codes, element 2i in the low nibble; N1 = 2I (SwiGLU:
+ *                        rows [0, I) gate, [I, 2I) up) or I (relu2)
+ *   s13 u8 [E, N1, ceil(H/G)]  E4M3 (NVFP4, G = 16) or E8M0 (MXFP4, G = 32) scale bytes
+ *   g13 f32 [E]          NVFP4 global dequant multiplier (ignored, may be NULL, for MXFP4)
+ *   w2  u8 [E, H, I/2], s2 u8 [E, H, ceil(I/G)], g2 f32 [E]   likewise for FC2.
+ * The prepared buffer is an opaque, lossless gfx950 layout: 16-row x 128-K fragments
+ * whose nibbles each lane reads with one 128-bit load in MFMA operand order, scales
+ * packed four K-blocks per 128-bit load, K and rows zero-padded to multiples of 128,
+ * SwiGLU gate and up row groups interleaved. */
+int moe_w4a16_prepared_size(const moe_w4a16_dims* dims, size_t* bytes);
+
+int moe_w4a16_prepare(const moe_w4a16_dims* dims, const uint8_t* w13, const uint8_t* s13,
+                      const float* g13, const uint8_t* w2, const uint8_t* s2, const float* g2,
+                      void* prepared, size_t prepared_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------ the fused layer
+ * Page: Description (fused FC1/FC2 kernel with cooperative persistent launches; a
+ * small-batch decode path that folds the top-k sum into the FC2 store epilogue),
+ * Performance (the m = 2048 stall: grid-wide barriers without co-residency),
+ * Reviewer Notes (decode path cap m <= 4 here, m <= 8 upstream).
+ *
+ * Tokens m <= MOE_DECODE_MAX_M take the decode path (split-K MFMA kernels with the
+ * top-k sum reduced in the FC2 workgroup, no atomics); larger m take the grouped
+ * GEMM path (FC1 + activation epilogue, FC2 with fp32 atomics of the weighted rows,
+ * a final bf16 cast). Neither path waits on a workgroup that may not be resident. */
+#define MOE_DECODE_MAX_M 16
+
+/* Workspace bytes for moe_w4a16_fused at a token capacity (route packing included). */
+int moe_w4a16_workspace_size(const moe_w4a16_dims* dims, int64_t token_capacity, int topk,
+                             size_t* bytes);
+
+/* x: device bf16 [m, H]; topk_ids: device int32 [m, topk]; topk_weights: device f32
+ * [m, topk]; expert_map: device int32 [num_global_experts] or NULL; out: device bf16
+ * [m, H], fully written (a token without a surviving route gets a zero row).
+ * prepared: the buffer filled by moe_w4a16_prepare for the same dims. m may be 0. */
+int moe_w4a16_fused(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes,
+                    const uint16_t* x, int64_t m, const int32_t* topk_ids,
+                    const float* topk_weights, int topk, const int32_t* expert_map,
+                    int num_global_experts, int64_t token_capacity, void* workspace,
+                    size_t workspace_bytes, uint16_t* out, hipStream_t stream);
+
+/* ------------------------------------------------------------------ diagnostics */
+
+/* Message for the calling thread's last failing call ("" if none). */
+const char* moe_last_error(void);
+
+/* Path selection for tests and tuning: 0 = automatic (decode for m <= the decode
+ * threshold), 1 = force decode (m <= MOE_DECODE_MAX_M), 2 = force grouped GEMM.
+ * Process-wide; the environment variable MOE_W4A16_FORCE_PATH=decode|gemm sets the
+ * initial value. Returns the previous value, or MOE_ERR_INVALID_ARG. */
+int moe_w4a16_set_path(int path);
+
+/* Decode threshold (default 8; MOE_W4A16_DECODE_MAX_M overrides it at load).
+ * Values outside [0, MOE_DECODE_MAX_M] are rejected. Returns the previous value. */
+int moe_w4a16_set_decode_max_m(int max_m);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

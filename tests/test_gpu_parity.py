@@ -1,0 +1,329 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Route packing must be bit-exact; the prepared weights must invert byte-exactly to the
+canonical codes; the fused layer must satisfy max|gpu - oracle| <= 2e-2 max|oracle| + 1e-3
+in bf16 on every workload shape, on the default dispatch and with each path forced.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from _common import SCALED, bf16_tensor_to_f64, dev, make_case, make_layer, oracle_out, run_layer
+from oracle import moe as M
+from oracle import route_pack as RP
+from synth import configs as C
+from synth import draw as D
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    d = torch.device("cuda:0")
+    torch.cuda.set_device(d)
+    return d
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import fp4_weight_grouped_moe_amd as m
+    yield m
+    m.moe_w4a16_set_path("auto")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ----------------------------------------------------------------------------- route packing
+
+def _gpu_route_pack(moe, device, ids, emap, eg, E, B, cap, ws=None):
+    k = ids.shape[1]
+    nbytes = moe.moe_route_pack_workspace_size(cap, k, E, B)
+    if ws is None:
+        ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device=device)   # garbage: result must not depend on it
+    d_ids = dev(ids.astype(np.int32), device)
+    d_map = dev(emap.astype(np.int32), device) if emap is not None else None
+    view = moe.moe_route_pack(d_ids, ids.shape[0], k, d_map, eg, E, B, cap, ws, nbytes)
+    torch.cuda.synchronize()
+    base = ws.data_ptr()
+
+    def read(ptr, n):
+        off = ptr - base
+        return ws[off:off + 4 * n].view(torch.int32).cpu().numpy().copy()
+
+    return {
+        "expert_counts": read(view.expert_counts, E),
+        "expert_offsets": read(view.expert_offsets, E + 1),
+        "sorted_route_ids": read(view.sorted_route_ids, view.cap_routes),
+        "block_expert": read(view.block_expert, view.cap_blocks),
+        "live": read(view.live, 4),
+        "route_slot": read(view.route_slot, cap * k),
+    }, ws
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "small", "prefill", "edge"])
+@pytest.mark.parametrize("block_m", [16, 32, 64, 128])
+def test_route_pack_bit_exact_full_configs(moe, device, name, block_m):
+    cfg = C.get_config(name)
+    for m in cfg.ms:
+        _say(f"route_pack {name} m={m} B={block_m}")
+        ids, _, emap, _ = D.draw_routing(cfg, m, seed=cfg.index)
+        cap = RP.token_capacity(m)
+        got, _ = _gpu_route_pack(moe, device, ids, emap, cfg.num_global_experts, cfg.num_experts, block_m, cap)
+        want = RP.route_pack(ids, emap, cfg.num_global_experts, cfg.num_experts, block_m, cap)
+        for key in want:
+            assert np.array_equal(got[key], want[key]), (name, m, block_m, key)
+
+
+def test_route_pack_capacity_reuse_one_workspace(moe, device):
+    cfg = C.get_config("edge")
+    ws = None
+    for m in (512, 300, 511):
+        _say(f"route_pack edge reuse m={m}")
+        ids, _, emap, _ = D.draw_routing(cfg, m, seed=10 + m)
+        got, ws = _gpu_route_pack(moe, device, ids, emap, cfg.num_global_experts, cfg.num_experts, 16, 512, ws)
+        want = RP.route_pack(ids, emap, cfg.num_global_experts, cfg.num_experts, 16, 512)
+        for key in want:
+            assert np.array_equal(got[key], want[key]), (m, key)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_route_pack_edge_cases(moe, device, seed):
+    rng = np.random.default_rng(100 + seed)
+    cases = [
+        (np.zeros((0, 4), np.int32), None, 8, 8),                         # m = 0
+        (np.full((5, 3), -1, np.int32), None, 8, 8),                      # everything dropped
+        (np.full((7, 4), 2, np.int32), None, 8, 8),                       # one expert, duplicates
+        (rng.integers(-3, 40, (33, 6)).astype(np.int32), rng.integers(-1, 20, 36).astype(np.int32), 36, 17),
+        (rng.integers(0, 3, (1000, 8)).astype(np.int32), None, 3, 3),     # heavy skew, several chunks
+    ]
+    ids, emap, eg, E = cases[seed % len(cases)]
+    B = [16, 32, 64, 128][seed % 4]
+    cap = RP.token_capacity(ids.shape[0])
+    _say(f"route_pack edge case {seed} m={ids.shape[0]} B={B}")
+    got, _ = _gpu_route_pack(moe, device, ids, emap, eg, E, B, cap)
+    want = RP.route_pack(ids, emap, eg, E, B, cap)
+    for key in want:
+        assert np.array_equal(got[key], want[key]), key
+
+
+# ----------------------------------------------------------------------------- prepare inverse
+
+def _invert_prepared(buf: np.ndarray, cfg: C.Workload):
+    """Canonical codes back from the prepared bytes, written from the documented layout."""
+    E, H, I = cfg.num_experts, cfg.hidden, cfg.inter
+    hp, ip = -(-H // 128) * 128, -(-I // 128) * 128
+    swiglu = cfg.act == "silu_swiglu"
+    n1g = (2 if swiglu else 1) * ip // 16
+    n2g = hp // 16
+    kb1, kb2 = hp // 128, ip // 128
+    nv = cfg.fmt == "nvfp4"
+    chunk = 512 if nv else 256
+
+    def a256(v):
+        return (v + 255) // 256 * 256
+
+    sc1pg = -(-kb1 // 4) * chunk
+    sc2pg = -(-kb2 // 4) * chunk
+    o_n1 = 0
+    o_s1 = a256(o_n1 + E * n1g * kb1 * 1024)
+    o_n2 = a256(o_s1 + E * n1g * sc1pg)
+    o_s2 = a256(o_n2 + E * n2g * kb2 * 1024)
+    o_g13 = a256(o_s2 + E * n2g * sc2pg)
+    o_g2 = a256(o_g13 + 4 * E)
+
+    def nibbles(off, groups, kbs):
+        a = buf[off:off + E * groups * kbs * 1024].reshape(E, groups, kbs, 4, 16, 4, 4)   # kb, q, r, s, byte
+        a = a.transpose(0, 1, 4, 2, 5, 3, 6)                                               # E, g, r, kb, s, q, b
+        return a.reshape(E, groups * 16, kbs * 64)                                         # row, byte along K
+
+    def scales(off, groups, per_group):
+        nch = per_group // chunk
+        a = buf[off:off + E * groups * per_group]
+        if nv:
+            a = a.reshape(E, groups, nch, 2, 16, 4, 4).transpose(0, 1, 4, 2, 5, 6, 3)     # r, ch, kbm, s, h
+            return a.reshape(E, groups * 16, nch * 32)
+        a = a.reshape(E, groups, nch, 16, 4, 4).transpose(0, 1, 3, 2, 4, 5)               # r, ch, kbm, s
+        return a.reshape(E, groups * 16, nch * 16)
+
+    def fc1_rows(a):
+        if not swiglu:
+            return a[:, :I]
+        a = a.reshape(E, ip // 16, 2, 16, a.shape[-1]).transpose(0, 2, 1, 3, 4).reshape(E, 2, ip, a.shape[-1])
+        return a[:, :, :I].reshape(E, 2 * I, a.shape[-1])
+
+    G = 16 if nv else 32
+    n13 = fc1_rows(nibbles(o_n1, n1g, kb1))
+    s13 = fc1_rows(scales(o_s1, n1g, sc1pg))
+    n2 = nibbles(o_n2, n2g, kb2)[:, :H]
+    s2 = scales(o_s2, n2g, sc2pg)[:, :H]
+    out = {
+        "w13": n13[..., :H // 2], "s13": s13[..., :-(-H // G)],
+        "w2": n2[..., :I // 2], "s2": s2[..., :-(-I // G)],
+        "g13": buf[o_g13:o_g13 + 4 * E].view(np.float32), "g2": buf[o_g2:o_g2 + 4 * E].view(np.float32),
+        "pad_nib13": n13[..., H // 2:], "pad_nib2": n2[..., I // 2:],
+    }
+    return out
+
+
+@pytest.mark.parametrize("name", list(SCALED))
+def test_prepare_inverts_byte_exact(moe, device, name):
+    cfg = SCALED[name]
+    _say(f"prepare inverse {name}")
+    case = make_case(cfg, 1, seed=3, weights="random")
+    layer = make_layer(case, device)
+    torch.cuda.synchronize()
+    buf = layer.prepared.cpu().numpy()
+    inv = _invert_prepared(buf, cfg)
+    for key in ("w13", "s13", "w2", "s2"):
+        assert np.array_equal(inv[key], case.codes[key]), key
+    if cfg.fmt == "nvfp4":
+        assert np.array_equal(inv["g13"], case.codes["g13"]) and np.array_equal(inv["g2"], case.codes["g2"])
+    else:
+        assert np.all(inv["g13"] == 1.0) and np.all(inv["g2"] == 1.0)
+    assert not inv["pad_nib13"].any() and not inv["pad_nib2"].any()
+
+
+# ----------------------------------------------------------------------------- fused layer
+
+def _check(case, got, tokens=None, cols=None, label=""):
+    ref = oracle_out(case, tokens=tokens, cols=cols)
+    if tokens is not None or cols is not None:
+        t = np.arange(case.m) if tokens is None else np.asarray(tokens)
+        c = np.arange(case.cfg.hidden) if cols is None else np.asarray(cols)
+        got = got[np.ix_(t, c)]
+    ok, err, bound = M.within_tolerance(got, ref)
+    _say(f"  {label}: max|err| = {err:.3e}, bound = {bound:.3e}, max|ref| = {np.max(np.abs(ref)):.3e}")
+    assert ok, f"{label}: {err} > {bound}"
+
+
+FUSED_CASES = [("tiny", 4), ("decode_s", 1), ("decode_s", 4), ("decode_s", 8), ("decode_s", 16),
+               ("small_s", 16), ("small_s", 64), ("prefill_s", 300), ("edge_s", 100)]
+
+
+@pytest.mark.parametrize("name,m", FUSED_CASES)
+@pytest.mark.parametrize("path", ["auto", "decode", "gemm"])
+def test_fused_matches_oracle_scaled(moe, device, name, m, path):
+    if path == "decode" and m > moe.MOE_DECODE_MAX_M:
+        pytest.skip("decode path serves m <= 16")
+    cfg = SCALED[name]
+    _say(f"fused {name} m={m} path={path}")
+    case = make_case(cfg, m, seed=cfg.index * 7 + m, weights="normal")
+    layer = make_layer(case, device)
+    moe.moe_w4a16_set_path(path)
+    try:
+        out = run_layer(layer, case, device)
+    finally:
+        moe.moe_w4a16_set_path("auto")
+    _check(case, bf16_tensor_to_f64(out), label=f"{name} m={m} {path}")
+
+
+def test_fused_capacity_reuse_one_workspace(moe, device):
+    cfg = SCALED["edge_s"]
+    case0 = make_case(cfg, 128, seed=41, weights="normal")
+    layer = make_layer(case0, device, token_capacity=128)
+    for m in (128, 100, 63, 64, 1):
+        _say(f"fused edge_s reuse cap=128 m={m}")
+        ids, w, emap, rng = D.draw_routing(cfg, m, seed=50 + m)
+        xbits = D.draw_activations_bf16(rng, m, cfg.hidden)
+        case = type(case0)(cfg, m, ids, w, emap, xbits, case0.codes)
+        out = run_layer(layer, case, device)
+        _check(case, bf16_tensor_to_f64(out), label=f"reuse m={m}")
+
+
+def test_fused_hand_cases(moe, device):
+    import json
+    import os
+
+    from test_oracle_moe import build_hand_case
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "moe_hand_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    import fp4_weight_grouped_moe_amd as m_
+
+    for hc in cases:
+        x, codes = build_hand_case(hc)
+        from oracle import formats as F
+        xbits = np.zeros(x.shape, np.uint16)
+        xbits[x == 1.0] = 0x3F80
+        cfg = C.Workload(name=hc["name"], index=0, num_experts=1, num_global_experts=1, hidden=hc["hidden"],
+                         inter=hc["inter"], topk=1, ms=(1,), fmt=hc["fmt"], act=hc["act"], routing="softmax")
+        if cfg.hidden % 8:
+            continue
+        for path in ("decode", "gemm"):
+            _say(f"hand case {hc['name']} path={path}")
+            from _common import Case
+            case = Case(cfg, 1, np.array(hc["topk_ids"], np.int32), np.array(hc["topk_weights"], np.float32), None,
+                        xbits, codes)
+            layer = make_layer(case, device)
+            m_.moe_w4a16_set_path(path)
+            try:
+                out = run_layer(layer, case, device)
+            finally:
+                m_.moe_w4a16_set_path("auto")
+            got = bf16_tensor_to_f64(out)
+            assert np.all(got == hc["expect_bf16"]), (hc["name"], path, got)
+
+
+def test_fused_dropped_tokens_are_zero_and_m0(moe, device):
+    cfg = SCALED["prefill_s"]
+    case = make_case(cfg, 40, seed=5, weights="normal")
+    case.ids[3, :] = -1
+    case.ids[17, :] = 1000
+    layer = make_layer(case, device)
+    for path in ("decode", "gemm"):
+        if path == "decode" and case.m > 16:
+            continue
+        moe.moe_w4a16_set_path(path)
+        try:
+            out = run_layer(layer, case, device)
+        finally:
+            moe.moe_w4a16_set_path("auto")
+        got = bf16_tensor_to_f64(out)
+        assert np.all(got[3] == 0) and np.all(got[17] == 0)
+        _check(case, got, label=f"dropped rows {path}")
+    # m = 0 is a no-op that succeeds
+    x = torch.empty((0, cfg.hidden), dtype=torch.bfloat16, device=device)
+    e = torch.empty((0, cfg.topk), dtype=torch.int32, device=device)
+    w = torch.empty((0, cfg.topk), dtype=torch.float32, device=device)
+    out = layer(x, e, w)
+    torch.cuda.synchronize()
+    assert out.shape == (0, cfg.hidden)
+
+
+# ----------------------------------------------------------------------------- full-size, sampled
+
+def _full_case(name, m, device, codes_dev=None):
+    cfg = C.get_config(name)
+    case = make_case(cfg, m, seed=cfg.index * 1000 + m, weights="none")
+    case.codes_dev = codes_dev if codes_dev is not None else D.draw_random_codes_torch(cfg, seed=1000 + cfg.index,
+                                                                                        device=device)
+    return case
+
+
+@pytest.mark.parametrize("name,ms", [("decode", (1, 4, 8)), ("small", (16, 64)), ("prefill", (2048,)),
+                                     ("edge", (512, 300, 511))])
+def test_fused_full_size_sampled(moe, device, name, ms):
+    cfg = C.get_config(name)
+    cap = max(RP.token_capacity(m) for m in ms)
+    case0 = _full_case(name, ms[0], device)
+    layer = make_layer(case0, device, token_capacity=cap)
+    rng = np.random.default_rng(7)
+    for m in ms:
+        case = _full_case(name, m, device, case0.codes_dev) if m != ms[0] else case0
+        _say(f"full {name} m={m} (capacity {cap})")
+        out = run_layer(layer, case, device)
+        got = bf16_tensor_to_f64(out)
+        tokens = np.unique(np.array([0, m - 1, rng.integers(0, m)]))
+        cols = np.sort(rng.choice(cfg.hidden, size=96, replace=False))
+        _check(case, got, tokens=tokens, cols=cols, label=f"{name} m={m}")
+        assert np.all(np.isfinite(got))
+    del layer, case0
+    torch.cuda.empty_cache()
