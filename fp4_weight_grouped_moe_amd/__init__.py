@@ -52,6 +52,14 @@ class moe_route_pack_view(ctypes.Structure):
 
 
 def _load():
+    # torch wheels bundle their own libamdhip64 with the same soname as ROCm's. Loading
+    # torch first makes this library bind to that runtime; the other order would put two
+    # HIP runtimes in the process, and torch's streams and pointers would not be valid in
+    # the one the kernels launch on.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
                           "(hipcc, gfx950). There is no CPU fallback.")
@@ -67,6 +75,7 @@ def _load():
         "moe_w4a16_prepare": (I32, [PD, P, P, P, P, P, P, P, SZ, P]),
         "moe_w4a16_workspace_size": (I32, [PD, I64, I32, PSZ]),
         "moe_w4a16_fused": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
+        "moe_w4a16_fused_profiled": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P, P, I32]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_w4a16_set_path": (I32, [I32]),
         "moe_w4a16_set_decode_max_m": (I32, [I32]),
@@ -81,7 +90,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("moe_route_pack_token_capacity", "moe_route_pack_workspace_size", "moe_route_pack",
             "moe_w4a16_prepared_size", "moe_w4a16_prepare", "moe_w4a16_workspace_size", "moe_w4a16_fused",
-            "moe_last_error", "moe_w4a16_set_path", "moe_w4a16_set_decode_max_m")
+            "moe_w4a16_fused_profiled", "moe_last_error", "moe_w4a16_set_path", "moe_w4a16_set_decode_max_m")
 
 
 def lib():
@@ -167,6 +176,17 @@ def moe_w4a16_fused(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: i
     _check(_lib.moe_w4a16_fused(ctypes.byref(dims), _ptr(prepared), prepared_bytes, _ptr(x), m, _ptr(topk_ids),
                                 _ptr(topk_weights), topk, _ptr(expert_map), num_global_experts, token_capacity,
                                 _ptr(workspace), workspace_bytes, _ptr(out), _stream(stream)), "moe_w4a16_fused")
+
+
+def moe_w4a16_fused_profiled(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: int, topk_ids, topk_weights,
+                             topk: int, expert_map, num_global_experts: int, token_capacity: int, workspace,
+                             workspace_bytes: int, out, events, stream=None) -> None:
+    """``events``: five or more torch.cuda.Event(enable_timing=True); their HIP handles are passed down."""
+    arr = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
+    _check(_lib.moe_w4a16_fused_profiled(ctypes.byref(dims), _ptr(prepared), prepared_bytes, _ptr(x), m,
+                                         _ptr(topk_ids), _ptr(topk_weights), topk, _ptr(expert_map),
+                                         num_global_experts, token_capacity, _ptr(workspace), workspace_bytes,
+                                         _ptr(out), _stream(stream), arr, len(events)), "moe_w4a16_fused_profiled")
 
 
 def moe_w4a16_set_path(path) -> int:

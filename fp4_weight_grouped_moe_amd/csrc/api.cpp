@@ -181,6 +181,8 @@ int moe_route_pack(const int32_t* topk_ids, int64_t m, int topk, const int32_t* 
   rp.slot_info = nullptr;
   rp.acc = nullptr;
   rp.acc_elems = 0;
+  rp.zero_ints = nullptr;
+  rp.n_zero_ints = 0;
   out->expert_counts = rp.expert_counts;
   out->expert_offsets = rp.expert_offsets;
   out->sorted_route_ids = rp.sorted_route_ids;
@@ -231,10 +233,14 @@ int moe_w4a16_workspace_size(const moe_w4a16_dims* dims, int64_t token_capacity,
   return ok();
 }
 
-int moe_w4a16_fused(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes, const uint16_t* x,
-                    int64_t m, const int32_t* topk_ids, const float* topk_weights, int topk,
-                    const int32_t* expert_map, int num_global_experts, int64_t token_capacity, void* workspace,
-                    size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes, const uint16_t* x, int64_t m,
+               const int32_t* topk_ids, const float* topk_weights, int topk, const int32_t* expert_map,
+               int num_global_experts, int64_t token_capacity, void* workspace, size_t workspace_bytes, uint16_t* out,
+               hipStream_t stream, hipEvent_t* events) {
   if (int rc = check_dims(dims)) return rc;
   if (int rc = check_pack_args(token_capacity, topk, dims->num_experts, kBlockM)) return rc;
   if (m < 0 || m > token_capacity)
@@ -256,9 +262,10 @@ int moe_w4a16_fused(const moe_w4a16_dims* dims, const void* prepared, size_t pre
     path = g_path;
     dmax = g_decode_max_m;
   }
-  const bool decode = path == 1 || (path == 0 && m <= dmax);
-  if (decode && m > MOE_DECODE_MAX_M)
-    return fail(MOE_ERR_UNSUPPORTED, "decode path forced for m = %lld > %d", (long long)m, MOE_DECODE_MAX_M);
+  const bool decode = path == 1 || (path == 0 && m <= dmax && token_capacity <= kDecodeMaxM);
+  if (decode && token_capacity > kDecodeMaxM)
+    return fail(MOE_ERR_UNSUPPORTED, "decode path needs token_capacity <= %d (got %lld)", kDecodeMaxM,
+                (long long)token_capacity);
   int cus = 0;
   if (int rc = check_device(&cus)) return rc;
   if (m == 0) return ok();
@@ -289,6 +296,8 @@ int moe_w4a16_fused(const moe_w4a16_dims* dims, const void* prepared, size_t pre
   rp.slot_info = reinterpret_cast<int2*>(pk + pg.off_tok_of_slot);
   rp.acc = decode ? nullptr : reinterpret_cast<float*>(ws + fg.off_acc);
   rp.acc_elems = decode ? 0 : m * dims->hidden;
+  rp.zero_ints = decode ? reinterpret_cast<int32_t*>(ws + fg.off_arrivals) : nullptr;
+  rp.n_zero_ints = decode ? fg.n_arrivals : 0;
 
   FusedParams fp{};
   const uint8_t* pw = static_cast<const uint8_t*>(prepared);
@@ -308,14 +317,42 @@ int moe_w4a16_fused(const moe_w4a16_dims* dims, const void* prepared, size_t pre
   fp.live = rp.live;
   fp.tiles = rp.tiles;
   fp.slot_info = rp.slot_info;
+  fp.route_slot = rp.route_slot;
   fp.inter = reinterpret_cast<uint16_t*>(ws + fg.off_inter);
   fp.acc = rp.acc;
+  fp.ybuf = reinterpret_cast<float*>(ws + fg.off_ybuf);
+  fp.fc2_arrivals = reinterpret_cast<int32_t*>(ws + fg.off_arrivals);
   fp.cap_blocks = pg.cap_blocks;
 
+  if (events) (void)hipEventRecord(events[0], stream);
   if (hipError_t e = launch_route_pack(rp, decode ? 0 : cus, stream); e != hipSuccess)
     return launch_status(e, "route pack launch");
-  hipError_t e = decode ? launch_decode(fp, cus, stream) : launch_gemm(fp, cus, stream);
+  if (events) (void)hipEventRecord(events[1], stream);
+  hipEvent_t* marks = events ? events + 2 : nullptr;
+  hipError_t e = decode ? launch_decode(fp, cus, stream, marks) : launch_gemm(fp, cus, stream, marks);
   return launch_status(e, decode ? "decode launch" : "grouped GEMM launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_w4a16_fused(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes, const uint16_t* x,
+                    int64_t m, const int32_t* topk_ids, const float* topk_weights, int topk,
+                    const int32_t* expert_map, int num_global_experts, int64_t token_capacity, void* workspace,
+                    size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
+  return fused_impl(dims, prepared, prepared_bytes, x, m, topk_ids, topk_weights, topk, expert_map,
+                    num_global_experts, token_capacity, workspace, workspace_bytes, out, stream, nullptr);
+}
+
+int moe_w4a16_fused_profiled(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes,
+                             const uint16_t* x, int64_t m, const int32_t* topk_ids, const float* topk_weights,
+                             int topk, const int32_t* expert_map, int num_global_experts, int64_t token_capacity,
+                             void* workspace, size_t workspace_bytes, uint16_t* out, hipStream_t stream,
+                             hipEvent_t* events, int num_events) {
+  if (!events || num_events < 5) return fail(MOE_ERR_INVALID_ARG, "events must hold at least 5 HIP events");
+  return fused_impl(dims, prepared, prepared_bytes, x, m, topk_ids, topk_weights, topk, expert_map,
+                    num_global_experts, token_capacity, workspace, workspace_bytes, out, stream, events);
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }

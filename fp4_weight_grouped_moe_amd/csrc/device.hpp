@@ -83,6 +83,15 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+// Workgroup barrier that orders LDS only. __syncthreads() also waits for every outstanding
+// global load of the wave (gfx9 counts loads and stores in one vmcnt), which would drain
+// the weight prefetch; LDS hand-offs between waves need only lgkmcnt.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float silu_f32(float z) {
   // z * sigmoid(z) with the hardware exp2 and reciprocal; the oracle uses exact exp and the
   // bf16 tolerance absorbs the few-ulp difference.

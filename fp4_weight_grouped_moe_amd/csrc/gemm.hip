@@ -262,25 +262,26 @@ hipError_t allow_large_lds(size_t lds) {
   return once;
 }
 
-hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream) {
+hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks) {
   // One 4-wave workgroup per CU: 128 accumulator AGPRs + ~230 VGPRs per wave leave room for one.
   const int grid = ((num_cus + kXcds - 1) / kXcds) * kXcds;
   const size_t lds = size_t(2) * kLdsBuf * sizeof(uint16_t);
   hipError_t e = p.g.fmt == FMT_NVFP4 ? allow_large_lds<FMT_NVFP4, 1>(lds) : allow_large_lds<FMT_MXFP4, 1>(lds);
   if (e == hipSuccess) e = p.g.fmt == FMT_NVFP4 ? allow_large_lds<FMT_NVFP4, 2>(lds) : allow_large_lds<FMT_MXFP4, 2>(lds);
   if (e != hipSuccess) return e;
-  if (p.g.fmt == FMT_NVFP4) {
-    hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 1>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
-    hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
-  } else {
-    hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 1>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
-    hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
-  }
+  const bool nv = p.g.fmt == FMT_NVFP4;
+  if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 1>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
+  else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 1>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
+  if (marks) (void)hipEventRecord(marks[0], stream);
+  if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
+  else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
+  if (marks) (void)hipEventRecord(marks[1], stream);
   const int64_t n = p.m * p.g.H;
   int64_t fb = (n / 2 + 255) / 256;
   if (fb < 1) fb = 1;
   if (fb > 4096) fb = 4096;
   hipLaunchKernelGGL(finalize_kernel, dim3(fb), dim3(256), 0, stream, p.acc, p.out, n);
+  if (marks) (void)hipEventRecord(marks[2], stream);
   return hipGetLastError();
 }
 

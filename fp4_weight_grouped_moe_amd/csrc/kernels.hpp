@@ -24,6 +24,8 @@ struct RoutePackParams {
   int2* slot_info;               // [cap_routes] (token, router weight bits) or null
   float* acc;                    // fp32 accumulator cleared by the extra workgroups, or null
   int64_t acc_elems;
+  int32_t* zero_ints;            // counters cleared by the packing workgroup, or null
+  int64_t n_zero_ints;
 };
 
 struct PrepareParams {
@@ -55,15 +57,21 @@ struct FusedParams {
   const int32_t* live;
   const int2* tiles;
   const int2* slot_info;
+  const int32_t* route_slot;      // [m * topk] packed slot of each route or -1
   uint16_t* inter;               // bf16 [cap_routes, ip]
-  float* acc;                    // fp32 [m, H]
+  float* acc;                    // fp32 [m, H] (grouped GEMM)
+  float* ybuf;                   // fp32 [cap_routes, hp] route partials (decode)
+  int32_t* fc2_arrivals;         // [hp / 64] decode FC2 arrival counters, zero on entry
   int64_t cap_blocks;
+  int64_t lds_block_table;       // decode FC1: bytes of LDS before the staged activations
 };
 
 size_t route_pack_lds_bytes(int num_experts);
 hipError_t launch_route_pack(const RoutePackParams& p, int zero_blocks, hipStream_t stream);
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
-hipError_t launch_decode(const FusedParams& p, int num_cus, hipStream_t stream);
-hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream);
+// `marks` (nullable) receives an event record after each kernel: FC1, FC2, final cast
+// (the decode path records its last mark right after FC2).
+hipError_t launch_decode(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks);
+hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks);
 
 }  // namespace moe

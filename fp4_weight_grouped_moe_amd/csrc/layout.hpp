@@ -96,21 +96,30 @@ __host__ __device__ inline PackGeom make_pack_geom(int64_t cap, int64_t k, int64
   return p;
 }
 
-// Fused-layer workspace: route pack (block 16) + bf16 intermediate + fp32 output accumulator.
+constexpr int kDecodeMaxM = 16;          // token columns of the decode path
+constexpr int kDecodeStageBytes = 65536; // LDS for the decode kernels' staged activation rows
+constexpr int kFc2RangeRows = 64;        // hidden rows per decode FC2 arrival counter
+
+// Fused-layer workspace: route pack (block 16) + bf16 intermediate + fp32 output
+// accumulator (grouped GEMM) + fp32 route partials and arrival counters (decode, only when
+// the capacity admits the decode path).
 struct FusedGeom {
   PackGeom pack;
-  size_t off_pack, off_inter, off_acc, total;
-  int64_t inter_stride;     // elements per intermediate row (= ip)
+  size_t off_pack, off_inter, off_acc, off_ybuf, off_arrivals, total;
+  int64_t n_arrivals;
 };
 
 __host__ __device__ inline FusedGeom make_fused_geom(const PreparedGeom& w, int64_t cap, int64_t k) {
   FusedGeom f{};
   f.pack = make_pack_geom(cap, k, w.E, kBlockM);
-  f.inter_stride = w.ip;
+  const bool decode = cap <= kDecodeMaxM;
+  f.n_arrivals = decode ? ceil_div(w.hp, kFc2RangeRows) : 0;
   size_t o = 0;
-  f.off_pack = o;  o = align256(o + f.pack.total);
-  f.off_inter = o; o = align256(o + size_t(f.pack.cap_routes) * w.ip * 2);
-  f.off_acc = o;   o = align256(o + size_t(cap) * w.H * 4);
+  f.off_pack = o;     o = align256(o + f.pack.total);
+  f.off_inter = o;    o = align256(o + size_t(f.pack.cap_routes) * w.ip * 2);
+  f.off_acc = o;      o = align256(o + size_t(cap) * w.H * 4);
+  f.off_ybuf = o;     o = align256(o + (decode ? size_t(f.pack.cap_routes) * w.hp * 4 : 0));
+  f.off_arrivals = o; o = align256(o + size_t(f.n_arrivals) * 4);
   f.total = o;
   return f;
 }

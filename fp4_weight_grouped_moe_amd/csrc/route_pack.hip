@@ -56,20 +56,26 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.num_experts, B = p.block_m;
   int* cnt = reinterpret_cast<int*>(smem);                 // [E] counts, then running slot
-  int* wave_tot = cnt + E;                                 // [kPackWaves + 1]
+  int* wave_tot = cnt + E;                                 // [32] scan scratch; [20] = valid routes
   uint8_t* wcnt = reinterpret_cast<uint8_t*>(wave_tot + 32);  // [kPackWaves][E] per-wave counts
 
+  // The first chunk's local id and router weight stay in registers for the scatter, so
+  // small batches read topk_ids / expert_map / topk_weights from memory only once.
+  const int l_first = local_expert(p, tid);
+  const float w_first = (p.topk_weights && tid < p.num_routes) ? p.topk_weights[tid] : 0.f;
   for (int e = tid; e < E; e += kPackThreads) cnt[e] = 0;
   if (tid == 0) wave_tot[kPackWaves + 4] = 0;
   for (int i = tid; i < kPackWaves * E; i += kPackThreads) wcnt[i] = 0;
+  for (int64_t i = tid; i < p.n_zero_ints; i += kPackThreads) p.zero_ints[i] = 0;
   __syncthreads();
-  for (int64_t r = tid; r < p.num_routes; r += kPackThreads) {
+  if (l_first >= 0) atomicAdd(&cnt[l_first], 1);
+  for (int64_t r = kPackThreads + tid; r < p.num_routes; r += kPackThreads) {
     int l = local_expert(p, r);
     if (l >= 0) atomicAdd(&cnt[l], 1);
   }
   __syncthreads();
 
-  // Padded segment offsets and the M-tile table, two experts per pass of the scan.
+  // Padded segment offsets and the M-tile table, kPackThreads experts per pass of the scan.
   int carry = 0, tile_carry = 0;
   for (int base = 0; base < E; base += kPackThreads) {
     int e = base + tid;
@@ -94,12 +100,10 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
           p.tiles[toff + t] = make_int2(first, nb | (e << 8));
         }
       }
+      cnt[e] = off;                                        // running slot of expert e
     }
-    __syncthreads();
-    if (e < E) cnt[e] = off;                               // running slot of expert e
     carry += tot;
     tile_carry += ttot;
-    __syncthreads();
   }
   const int total_padded = carry;
   if (tid == 0) {
@@ -115,6 +119,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   }
   for (int64_t b = total_padded / B + tid; b < p.cap_blocks; b += kPackThreads) p.block_expert[b] = -1;
   for (int64_t r = p.num_routes + tid; r < p.cap_k; r += kPackThreads) p.route_slot[r] = -1;
+  __syncthreads();
 
   // Stable scatter, 1024 routes per chunk: rank inside the wave by matching equal expert
   // ids, then add the counts of lower waves of the chunk and the running slot.
@@ -122,7 +127,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t base = 0; base < p.num_routes; base += kPackThreads) {
     const int64_t r = base + tid;
-    const int l = local_expert(p, r);
+    const int l = base == 0 ? l_first : local_expert(p, r);
     int rank = 0;
     uint64_t todo = __ballot(l >= 0);
     valid_total += __popcll(todo);
@@ -143,22 +148,24 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
       p.sorted_route_ids[pos] = int(r);
       p.route_slot[r] = pos;
       if (p.slot_info) {
-        float wt = p.topk_weights ? p.topk_weights[r] : 0.f;
+        const float wt = base == 0 ? w_first : (p.topk_weights ? p.topk_weights[r] : 0.f);
         p.slot_info[pos] = make_int2(int(r / p.topk), __float_as_int(wt));
       }
     } else if (r < p.num_routes) {
       p.route_slot[r] = -1;
     }
-    __syncthreads();
-    for (int e = tid; e < E; e += kPackThreads) {
-      int add = 0;
-      for (int w2 = 0; w2 < kPackWaves; ++w2) {
-        add += wcnt[w2 * E + e];
-        wcnt[w2 * E + e] = 0;
+    if (base + kPackThreads < p.num_routes) {                // more chunks: advance the running slots
+      __syncthreads();
+      for (int e = tid; e < E; e += kPackThreads) {
+        int add = 0;
+        for (int w2 = 0; w2 < kPackWaves; ++w2) {
+          add += wcnt[w2 * E + e];
+          wcnt[w2 * E + e] = 0;
+        }
+        cnt[e] += add;
       }
-      cnt[e] += add;
+      __syncthreads();
     }
-    __syncthreads();
   }
   // valid_total is per wave (ballots are wave-wide); lane 0 of each wave adds its share.
   if (lane == 0) atomicAdd(&wave_tot[kPackWaves + 4], valid_total);

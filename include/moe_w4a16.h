@@ -141,10 +141,13 @@ int moe_w4a16_prepare(const moe_w4a16_dims* dims, const uint8_t* w13, const uint
  * Performance (the m = 2048 stall: grid-wide barriers without co-residency),
  * Reviewer Notes (decode path cap m <= 4 here, m <= 8 upstream).
  *
- * Tokens m <= MOE_DECODE_MAX_M take the decode path (split-K MFMA kernels with the
- * top-k sum reduced in the FC2 workgroup, no atomics); larger m take the grouped
- * GEMM path (FC1 + activation epilogue, FC2 with fp32 atomics of the weighted rows,
- * a final bf16 cast). Neither path waits on a workgroup that may not be resident. */
+ * A call whose m is at most the decode threshold and whose token_capacity is at most
+ * MOE_DECODE_MAX_M takes the decode path: split-K MFMA kernels, route partials in fp32,
+ * and the last FC2 workgroup of each hidden-row range (an atomic arrival count, never a
+ * wait) sums every token's routes in a fixed order -- deterministic, no atomics on data.
+ * Other calls take the grouped GEMM path: FC1 + activation epilogue, FC2 with fp32
+ * atomic adds of the weighted rows, a final bf16 cast. Neither path waits on a
+ * workgroup that may not be resident. */
 #define MOE_DECODE_MAX_M 16
 
 /* Workspace bytes for moe_w4a16_fused at a token capacity (route packing included). */
@@ -163,11 +166,23 @@ int moe_w4a16_fused(const moe_w4a16_dims* dims, const void* prepared, size_t pre
 
 /* ------------------------------------------------------------------ diagnostics */
 
+/* Measurement twin of moe_w4a16_fused: the same launches on `stream`, with HIP event
+ * records between them -- events[0] before route packing, [1] after it, [2] after FC1,
+ * [3] after FC2, [4] after the bf16 cast (decode path: [4] right after [3]). The
+ * caller creates the events (num_events >= 5). Not for graph capture. */
+int moe_w4a16_fused_profiled(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes,
+                             const uint16_t* x, int64_t m, const int32_t* topk_ids,
+                             const float* topk_weights, int topk, const int32_t* expert_map,
+                             int num_global_experts, int64_t token_capacity, void* workspace,
+                             size_t workspace_bytes, uint16_t* out, hipStream_t stream,
+                             hipEvent_t* events, int num_events);
+
 /* Message for the calling thread's last failing call ("" if none). */
 const char* moe_last_error(void);
 
 /* Path selection for tests and tuning: 0 = automatic (decode for m <= the decode
- * threshold), 1 = force decode (m <= MOE_DECODE_MAX_M), 2 = force grouped GEMM.
+ * threshold), 1 = force decode (token_capacity <= MOE_DECODE_MAX_M, else the call
+ * fails with MOE_ERR_UNSUPPORTED), 2 = force grouped GEMM.
  * Process-wide; the environment variable MOE_W4A16_FORCE_PATH=decode|gemm sets the
  * initial value. Returns the previous value, or MOE_ERR_INVALID_ARG. */
 int moe_w4a16_set_path(int path);

@@ -164,3 +164,15 @@ def test_path_and_threshold_setters():
     assert moe.moe_w4a16_set_decode_max_m(old) == 4
     with pytest.raises(moe.MoeError):
         moe.moe_w4a16_set_decode_max_m(17)
+
+
+def test_one_hip_runtime_in_process():
+    """The library must bind to the HIP runtime torch loaded, never a second copy."""
+    import subprocess
+    import sys
+    code = ("import fp4_weight_grouped_moe_amd, torch\n"
+            "libs = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(libs))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip() == "1", out.stdout
