@@ -42,7 +42,21 @@ def parse():
     ap.add_argument("--sweep", action="store_true", help="also report the workload's other token counts")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run three device copies of MIB MiB (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
+
+
+def copy_probe(mib):
+    import torch
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
 
 
 class HipEvents:
@@ -106,6 +120,9 @@ def load_traffic(kernel, workload, digest, per_launch_bytes):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
               "(the layer has no multi-GPU path here).", file=sys.stderr)

@@ -52,9 +52,11 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 // ----------------------------------------------------------------------------- FC1
 
+static_assert(kF1Slice == kScaleChunkKB, "one 16-byte scale load per fragment per FC1 unit");
+
 struct F1Unit {
-  u32x4 q0[kF1Slice], q1[kF1Slice];
-  uint32_t s0[kF1Slice], s1[kF1Slice];
+  u32x4 q0[kF1Slice], q1[kF1Slice];  // nibbles of the two row groups, one 1 KiB block per K block
+  u32x4 s0, s1;                      // their scales: dword j = the four MFMA steps of K block j
   int2 info;                         // (token, router weight) of this lane's route column
 };
 
@@ -64,83 +66,137 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
   __shared__ f32x4 red[kF1Waves][2][64];
   const PreparedGeom& g = p.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
-  const bool nv = FMT == FMT_NVFP4;
-  const int64_t H = g.H, xchunks = H / 8;
-  const int64_t live_blocks = p.live[2];
+  const int q = lane >> 4, col = lane & 15;
+  const int H = g.H, hp = int(g.hp);
+  const int xchunks = hp / 8;                                 // 16-byte chunks per staged row
+  const int live_blocks = p.live[2];
   int4* bt = reinterpret_cast<int4*>(dyn);                   // block -> (expert, g13, g2)
-  uint16_t* xs = reinterpret_cast<uint16_t*>(dyn + p.lds_block_table);   // [m][H], chunk-swizzled
+  int* sp = reinterpret_cast<int*>(dyn + p.lds_block_table - kDecodeMaxM * sizeof(int));   // per-token p
+  uint16_t* xs = reinterpret_cast<uint16_t*>(dyn + p.lds_block_table);   // [m][hp], chunk-swizzled
 
-  for (int64_t b = tid; b < live_blocks; b += kF1Threads) {
+  for (int b = tid; b < live_blocks; b += kF1Threads) {
     const int e = p.block_expert[b];
     bt[b] = make_int4(e, __float_as_int(p.g13[e]), __float_as_int(p.g2[e]), 0);
   }
+  // Activation rows in LDS, zero-padded to hp. Chunk j of row t sits at chunk j ^ (t & 7)
+  // (hp is a multiple of 128, so every group of 8 chunks is complete): lanes reading the
+  // same K of different tokens hit different banks.
+  // NVFP4 runs on the f16 MFMA: E2M1 x E4M3 weights are exact in f16, and each token's bf16
+  // row is rescaled by a power of two 2^-p (exact) so that its largest magnitude lies in
+  // [2^14, 2^15) before the f16 cast; the epilogue multiplies by 2^p again.
+  constexpr bool F16 = STAGED && FMT == FMT_NVFP4;
   if (STAGED) {
-    for (int64_t c = tid; c < p.m * xchunks; c += kF1Threads) {
-      const int64_t t = c / xchunks, j = c % xchunks;
-      *reinterpret_cast<u32x4*>(xs + t * H + swz(j, int(t), xchunks) * 8) =
-          *reinterpret_cast<const u32x4*>(p.x + t * H + j * 8);
+    for (int c = tid; c < p.m * xchunks; c += kF1Threads) {
+      const int t = c / xchunks, j = c % xchunks;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (j * 8 < H) v = *reinterpret_cast<const u32x4*>(p.x + int64_t(t) * H + j * 8);
+      *reinterpret_cast<u32x4*>(xs + t * hp + ((j ^ (t & 7)) << 3)) = v;
     }
   }
   lds_barrier();
+  if constexpr (F16) {
+    for (int t = wave; t < p.m; t += kF1Waves) {
+      float mx = 0.f;
+      for (int c = lane; c < xchunks; c += 64) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(xs + t * hp + c * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          mx = fmaxf(mx, fabsf(__uint_as_float(v[i] << 16)));
+          mx = fmaxf(mx, fabsf(__uint_as_float(v[i] & 0xFFFF0000u)));
+        }
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+      if (lane == 0) sp[t] = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 15 : 0;
+    }
+    lds_barrier();
+    for (int c = tid; c < p.m * xchunks; c += kF1Threads) {
+      const int t = c / xchunks;
+      const int neg = -sp[t];
+      u32x4* ptr = reinterpret_cast<u32x4*>(xs + t * hp + (c % xchunks) * 8);
+      const u32x4 v = *ptr;
+      f16x2 h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        h[i] = f16x2{(_Float16)ldexpf(__uint_as_float(v[i] << 16), neg),
+                     (_Float16)ldexpf(__uint_as_float(v[i] & 0xFFFF0000u), neg)};
+      *ptr = __builtin_bit_cast(u32x4, h);
+    }
+    lds_barrier();
+  }
 
-  const int64_t n_it = g.n1_groups / 2;                      // items per block: two row groups
-  const int64_t n_items = live_blocks * n_it;
-  const int64_t nsl = (g.kb1 + kF1Slice - 1) / kF1Slice;      // K slices per item
-  const int64_t spw = (nsl + kF1Waves - 1) / kF1Waves;        // slices per wave per item
-  const int64_t my_items = n_items > blockIdx.x ? (n_items - blockIdx.x + gridDim.x - 1) / gridDim.x : 0;
-  const int64_t U = my_items * spw;
-  const int64_t U2 = (U + 1) & ~int64_t(1);                  // even: the loop below takes units in pairs
-  const int col = lane & 15;
-
-  auto unit_item = [&](int64_t u) { return int64_t(blockIdx.x) + (u / spw) * gridDim.x; };
-  auto unit_slice = [&](int64_t u) { return wave + kF1Waves * (u % spw); };
+  const int n_it = int(g.n1_groups / 2);                      // items per block: two row groups
+  const int n_items = live_blocks * n_it;
+  const int nsl = int((g.kb1 + kF1Slice - 1) / kF1Slice);     // K slices per item
+  const int spw = (nsl + kF1Waves - 1) / kF1Waves;            // slices per wave per item
+  const int my_items = n_items > int(blockIdx.x) ? (n_items - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x) : 0;
+  const int U = my_items * spw;
+  const int U2 = (U + 1) & ~1;                                // even: units are taken in pairs
+  const int kb1 = int(g.kb1);
+  const int sc_lane = FMT == FMT_NVFP4 ? ((lane >> 5) * 16 + col) * 16 : col * 16;
 
   // Loads are unconditional so that the wait counters stay exact: units past the end and
-  // slices past K re-read a valid block (an L2 hit) whose contribution is masked.
-  auto issue = [&](int64_t u, F1Unit& r) {
-    u = min(u, U - 1);
-    const int64_t item = unit_item(u), sl = min(unit_slice(u), nsl - 1);
-    const int64_t blk = item / n_it, it = item % n_it;
+  // K blocks past kb1 re-read a valid block (an L2 hit) whose contribution is skipped.
+  // Base addresses are wave-uniform (scalar registers); lanes add a 32-bit offset.
+  auto issue = [&](int u, F1Unit& r) {
+    const int uu = min(u, U - 1);
+    const int item = int(blockIdx.x) + (uu / spw) * int(gridDim.x);
+    const int sl = min(wave + kF1Waves * (uu % spw), nsl - 1);
+    const int blk = item / n_it, it = item % n_it;
     r.info = p.slot_info[blk * kBlockM + col];
-    const int64_t gi = int64_t(bt[blk].x) * g.n1_groups + 2 * it;
-    const uint8_t* nb0 = p.nib1 + gi * g.kb1 * kFragBytes + lane * 16;
+    const int64_t gi = int64_t(uniform(bt[blk].x)) * g.n1_groups + 2 * it;
+    const uint8_t* nb0 = p.nib1 + gi * g.kb1 * kFragBytes;
     const uint8_t* nb1 = nb0 + g.kb1 * kFragBytes;
-    const uint8_t* sg0 = p.sc1 + gi * g.sc1_per_group;
-    const uint8_t* sg1 = sg0 + g.sc1_per_group;
 #pragma unroll
     for (int j = 0; j < kF1Slice; ++j) {
-      const int64_t kb = min(sl * kF1Slice + j, g.kb1 - 1);
-      r.q0[j] = *reinterpret_cast<const u32x4*>(nb0 + kb * kFragBytes);
-      r.q1[j] = *reinterpret_cast<const u32x4*>(nb1 + kb * kFragBytes);
-      r.s0[j] = scale_dword(sg0, kb, lane, nv);
-      r.s1[j] = scale_dword(sg1, kb, lane, nv);
+      const int kb = min(sl * kF1Slice + j, kb1 - 1);
+      r.q0[j] = *reinterpret_cast<const u32x4*>(nb0 + int64_t(kb) * kFragBytes + lane * 16);
+      r.q1[j] = *reinterpret_cast<const u32x4*>(nb1 + int64_t(kb) * kFragBytes + lane * 16);
     }
+    const uint8_t* sg0 = p.sc1 + gi * g.sc1_per_group + int64_t(sl) * g.sc_chunk_bytes;
+    r.s0 = *reinterpret_cast<const u32x4*>(sg0 + sc_lane);
+    r.s1 = *reinterpret_cast<const u32x4*>(sg0 + g.sc1_per_group + sc_lane);
   };
 
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](int64_t u, const F1Unit& r) {
-    const int64_t sl = unit_slice(u);
-    if (u < U && sl < nsl) {
-      const int tok = r.info.x;
+  auto compute = [&](int u, const F1Unit& r) {
+    if (u >= U) return;
+    const int sl = wave + kF1Waves * (u % spw);
+    if (sl >= nsl) return;
+    const int tok = r.info.x;
+    const int t = max(tok, 0);                                // padding columns read row 0; masked later
+    int xoff[4];
 #pragma unroll
-      for (int j = 0; j < kF1Slice; ++j) {
-        const int64_t kb = sl * kF1Slice + j;
+    for (int s = 0; s < 4; ++s) xoff[s] = t * hp + (((4 * s + q) ^ (t & 7)) << 3);
+#pragma unroll
+    for (int j = 0; j < kF1Slice; ++j) {
+      const int kb = sl * kF1Slice + j;
+      if (kb < kb1) {
+        float sa[4], sb[4];
+        decode_scales<FMT>(r.s0[j], sa);
+        decode_scales<FMT>(r.s1[j], sb);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const int64_t k = kb * kKBlock + 32 * s + 8 * (lane >> 4);
-          bf16x8 xb = zero_bf16x8();
-          if (tok >= 0 && k < H) {
-            if (STAGED) xb = load_bf16x8(xs + int64_t(tok) * H + swz(k >> 3, tok, xchunks) * 8);
-            else xb = load_bf16x8(p.x + int64_t(tok) * H + k);
+          if constexpr (F16) {
+            const f16x8 xb = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(xs + xoff[s] + kb * kKBlock));
+            acc0 = mfma16h(dq8_nv_f16(r.q0[j][s], split_nv_scale(sa[s])), xb, acc0);
+            acc1 = mfma16h(dq8_nv_f16(r.q1[j][s], split_nv_scale(sb[s])), xb, acc1);
+          } else {
+            bf16x8 xb;
+            if (STAGED) xb = load_bf16x8(xs + xoff[s] + kb * kKBlock);
+            else {
+              const int k = kb * kKBlock + 32 * s + 8 * q;
+              xb = (tok >= 0 && k < H) ? load_bf16x8(p.x + int64_t(tok) * H + k) : zero_bf16x8();
+            }
+            acc0 = mfma16(dq8<FMT>(r.q0[j][s], sa[s]), xb, acc0);
+            acc1 = mfma16(dq8<FMT>(r.q1[j][s], sb[s]), xb, acc1);
           }
-          acc0 = mfma16(dq8<FMT>(r.q0[j][s], (r.s0[j] >> (8 * s)) & 0xFF), xb, acc0);
-          acc1 = mfma16(dq8<FMT>(r.q1[j][s], (r.s1[j] >> (8 * s)) & 0xFF), xb, acc1);
         }
       }
     }
   };
 
-  auto finish = [&](int64_t u, const F1Unit& r) {
+  auto finish = [&](int u, const F1Unit& r) {
     if (u >= U || u % spw != spw - 1) return;                 // not the item's last slice
     red[wave][0][lane] = acc0;
     red[wave][1][lane] = acc1;
@@ -154,14 +210,16 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
         h0 += red[w][0][lane];
         h1 += red[w][1][lane];
       }
-      const int64_t item = unit_item(u);
-      const int64_t blk = item / n_it, it = item % n_it;
+      const int item = int(blockIdx.x) + (u / spw) * int(gridDim.x);
+      const int blk = item / n_it, it = item % n_it;
       const int4 b4 = bt[blk];
       const int tok = r.info.x;
-      const float g13 = __int_as_float(b4.y), g2 = __int_as_float(b4.z);
+      float g13 = __int_as_float(b4.y);
+      const float g2 = __int_as_float(b4.z);
+      if constexpr (F16) g13 = ldexpf(g13, tok >= 0 ? sp[tok] : 0);
       const float rw = (tok >= 0) ? __int_as_float(r.info.y) * g2 : 0.f;
-      uint16_t* dst = p.inter + (blk * kBlockM + col) * g.ip;
-      const int r0 = 4 * (lane >> 4);
+      uint16_t* dst = p.inter + int64_t(blk * kBlockM + col) * g.ip;
+      const int r0 = 4 * q;
       if (g.act == ACT_SWIGLU) {
         float a[4];
 #pragma unroll
@@ -182,10 +240,11 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
     lds_barrier();
   };
 
+  // Two register sets: the next unit's loads stay in flight while this one is computed.
   if (U == 0) return;
   F1Unit ra, rb;
   issue(0, ra);
-  for (int64_t u = 0; u < U2; u += 2) {
+  for (int u = 0; u < U2; u += 2) {
     issue(u + 1, rb);
     compute(u, ra);
     finish(u, ra);
@@ -198,9 +257,9 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
 // ----------------------------------------------------------------------------- FC2
 
 struct F2Unit {
-  u32x4 q[kF2Slice];
-  uint32_t s[kF2Slice];
-  bf16x8 b[kF2Slice][4];
+  u32x4 q[kF2Slice];                 // 1 KiB fragment blocks
+  uint2 s;                           // their scale dwords
+  bf16x8 b[kF2Slice][4];             // the route column's intermediate values for the MFMA steps
 };
 
 template <int FMT>
@@ -209,65 +268,76 @@ __global__ __launch_bounds__(kF2Threads, 1) void decode_fc2_kernel(FusedParams p
   __shared__ float tacc[kF2Waves][kDecodeMaxM][16];
   const PreparedGeom& g = p.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
-  const bool nv = FMT == FMT_NVFP4;
+  const int q = lane >> 4, col = lane & 15;
   const int64_t ht = blockIdx.x;                             // 16 hidden rows per workgroup
-  const int64_t live_blocks = p.live[2];
+  const int live_blocks = p.live[2];
   int* be = reinterpret_cast<int*>(dyn);                     // block -> expert
   int* stok = be + p.cap_blocks;                             // slot -> token (-1 = padding)
-  for (int64_t b = tid; b < live_blocks; b += kF2Threads) be[b] = p.block_expert[b];
-  for (int64_t s = tid; s < live_blocks * kBlockM; s += kF2Threads) stok[s] = p.slot_info[s].x;
+  for (int b = tid; b < live_blocks; b += kF2Threads) be[b] = p.block_expert[b];
+  for (int s = tid; s < live_blocks * kBlockM; s += kF2Threads) stok[s] = p.slot_info[s].x;
   for (int i = tid; i < kF2Waves * kDecodeMaxM * 16; i += kF2Threads) (&tacc[0][0][0])[i] = 0.f;
   lds_barrier();
 
-  const int64_t nsl = (g.kb2 + kF2Slice - 1) / kF2Slice;
-  const int64_t units = live_blocks * nsl;
-  const int64_t U = units > wave ? (units - wave + kF2Waves - 1) / kF2Waves : 0;
-  const int64_t U2 = (U + 1) & ~int64_t(1);
-  const int col = lane & 15;
+  static_assert(kScaleChunkKB % kF2Slice == 0, "an FC2 unit never straddles a scale chunk");
+  const int kb2 = int(g.kb2);
+  const int nsl = (kb2 + kF2Slice - 1) / kF2Slice;
+  const int units = live_blocks * nsl;                        // (route block, K slice) pairs
+  const int U = units > wave ? (units - wave + kF2Waves - 1) / kF2Waves : 0;
+  const int U2 = (U + 1) & ~1;
+  const int sc_lane = FMT == FMT_NVFP4 ? ((lane >> 5) * 16 + col) * 16 : col * 16;
 
-  // Unconditional loads (units past the end re-read the last one, masked) keep the wait
-  // counters exact across the ping-pong.
-  auto issue = [&](int64_t u, F2Unit& r) {
-    const int64_t unit = wave + min(u, U - 1) * kF2Waves;
-    const int64_t blk = unit / nsl, sl = unit % nsl;
-    const int64_t e = be[blk];
-    const uint8_t* nb = p.nib2 + ((e * g.n2_groups + ht) * g.kb2) * kFragBytes + lane * 16;
-    const uint8_t* sg = p.sc2 + (e * g.n2_groups + ht) * g.sc2_per_group;
-    const int64_t slot = blk * kBlockM + col;
-    const bool valid = stok[slot] >= 0;
-    const uint16_t* irow = p.inter + slot * g.ip + 8 * (lane >> 4);
+  // Weight loads are unconditional (units past the end re-read the last one, skipped);
+  // intermediate rows are loaded only for live route columns, so L2 traffic follows the
+  // routes, not the padded blocks.
+  auto issue = [&](int u, F2Unit& r) {
+    const int unit = wave + min(u, U - 1) * kF2Waves;
+    const int blk = unit / nsl, sl = unit % nsl;
+    const int64_t gi = int64_t(uniform(be[blk])) * g.n2_groups + ht;
+    const uint8_t* nb = p.nib2 + gi * g.kb2 * kFragBytes;
 #pragma unroll
     for (int j = 0; j < kF2Slice; ++j) {
-      const int64_t kb = sl * kF2Slice + j;
-      const int64_t kbc = min(kb, g.kb2 - 1);                 // clamped; masked through the B operand
-      r.q[j] = *reinterpret_cast<const u32x4*>(nb + kbc * kFragBytes);
-      r.s[j] = scale_dword(sg, kbc, lane, nv);
+      const int kb = min(sl * kF2Slice + j, kb2 - 1);
+      r.q[j] = *reinterpret_cast<const u32x4*>(nb + int64_t(kb) * kFragBytes + lane * 16);
+    }
+    const int kb0 = sl * kF2Slice;
+    r.s = *reinterpret_cast<const uint2*>(p.sc2 + gi * g.sc2_per_group + int64_t(kb0 / kScaleChunkKB) * g.sc_chunk_bytes +
+                                          sc_lane + (kb0 % kScaleChunkKB) * 4);
+    const int slot = blk * kBlockM + col;
+    const bool valid = stok[slot] >= 0;
+    const uint16_t* irow = p.inter + int64_t(slot) * g.ip + 8 * q;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        r.b[j][s] = (valid && kb < g.kb2) ? load_bf16x8(irow + kb * kKBlock + 32 * s) : zero_bf16x8();
+    for (int j = 0; j < kF2Slice; ++j) {
+      const int kb = min(sl * kF2Slice + j, kb2 - 1);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) r.b[j][s] = valid ? load_bf16x8(irow + kb * kKBlock + 32 * s) : zero_bf16x8();
     }
   };
-  auto compute = [&](int64_t u, const F2Unit& r) {
+  auto compute = [&](int u, const F2Unit& r) {
     if (u >= U) return;
-    const int64_t unit = wave + u * kF2Waves;
-    const int64_t blk = unit / nsl;
+    const int unit = wave + u * kF2Waves;
+    const int blk = unit / nsl, sl = unit % nsl;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < kF2Slice; ++j)
+    for (int j = 0; j < kF2Slice; ++j) {
+      if (sl * kF2Slice + j < kb2) {
+        float sc[4];
+        decode_scales<FMT>(j == 0 ? r.s.x : r.s.y, sc);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = mfma16(dq8<FMT>(r.q[j][s], (r.s[j] >> (8 * s)) & 0xFF), r.b[j][s], acc);
+        for (int s = 0; s < 4; ++s) acc = mfma16(dq8<FMT>(r.q[j][s], sc[s]), r.b[j][s], acc);
+      }
+    }
     const int tok = stok[blk * kBlockM + col];
     if (tok >= 0) {
-      const int r0 = 4 * (lane >> 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) atomicAdd(&tacc[wave][tok][r0 + i], acc[i]);
+      for (int i = 0; i < 4; ++i) atomicAdd(&tacc[wave][tok][4 * q + i], acc[i]);
     }
   };
 
+  // Two register sets: the next unit's loads stay in flight while this one is computed.
   if (U > 0) {
     F2Unit ra, rb;
     issue(0, ra);
-    for (int64_t u = 0; u < U2; u += 2) {
+    for (int u = 0; u < U2; u += 2) {
       issue(u + 1, rb);
       compute(u, ra);
       issue(u + 2, ra);
@@ -298,19 +368,20 @@ hipError_t allow_lds(K kernel, int bytes) {
 template <int FMT>
 hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t stream, hipEvent_t* marks) {
   static const hipError_t lds_ok = [] {
-    hipError_t e = allow_lds(&decode_fc1_kernel<FMT, true>, kDecodeStageBytes + 16384);
-    if (e == hipSuccess) e = allow_lds(&decode_fc1_kernel<FMT, false>, 16384);
-    if (e == hipSuccess) e = allow_lds(&decode_fc2_kernel<FMT>, 65536);
+    // dynamic LDS: block table (<= 1024 blocks at capacity 16) + staged rows / slot tokens
+    hipError_t e = allow_lds(&decode_fc1_kernel<FMT, true>, kDecodeStageBytes + 32768);
+    if (e == hipSuccess) e = allow_lds(&decode_fc1_kernel<FMT, false>, 32768);
+    if (e == hipSuccess) e = allow_lds(&decode_fc2_kernel<FMT>, 98304);
     return e;
   }();
   if (lds_ok != hipSuccess) return lds_ok;
   FusedParams p = p0;
   const PreparedGeom& g = p.g;
-  const size_t table = align256(size_t(p.cap_blocks) * sizeof(int4));
+  const size_t table = align256(size_t(p.cap_blocks) * sizeof(int4) + kDecodeMaxM * sizeof(int));
   p.lds_block_table = int64_t(table);
   const int64_t items = p.cap_blocks * (g.n1_groups / 2);
   const int64_t grid1 = max(int64_t(1), min(items, int64_t(num_cus) * 2));
-  const size_t xs_bytes = size_t(p.m) * g.H * 2;
+  const size_t xs_bytes = size_t(p.m) * g.hp * 2;
   if (xs_bytes <= size_t(kDecodeStageBytes))
     hipLaunchKernelGGL((decode_fc1_kernel<FMT, true>), dim3(grid1), dim3(kF1Threads), table + xs_bytes, stream, p);
   else

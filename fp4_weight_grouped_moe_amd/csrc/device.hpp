@@ -11,6 +11,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // D += A * B for a 16x16x32 bf16 step. Lane l holds A[l%16][8*(l/16) + j] and
 // B[8*(l/16) + j][l%16] (j = 0..7); D row 4*(l/16) + i, column l%16 in element i.
@@ -18,19 +20,32 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// E4M3FN byte -> float (OCP FP8): bias 7, exponent field 0 subnormal, S.1111.111 NaN.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  uint32_t mag = b & 0x7Fu;
-  float f = __uint_as_float((mag << 20) + (120u << 23));           // normal numbers
-  if ((mag & 0x78u) == 0) f = float(mag & 7u) * 0x1p-9f;            // subnormals (and zero)
-  if (mag == 0x7Fu) f = __uint_as_float(0x7FC00000u);
-  return (b & 0x80u) ? -f : f;
+// Same for the f16 MFMA (identical lane layout).
+__device__ __forceinline__ f32x4 mfma16h(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// E8M0 byte -> the float whose exponent field is that byte. The gfx950 scaled FP4
-// converts apply only the exponent of their f32 scale operand, so this is exactly
-// 2^(b-127) as far as they are concerned (b = 0 gives 2^-127, b = 255 NaN/inf).
-__device__ __forceinline__ float e8m0_as_scale(uint32_t b) { return __uint_as_float(b << 23); }
+// Four scale bytes of one K block (byte s = the scale of MFMA step s) -> four floats.
+// NVFP4: OCP E4M3FN values, decoded by the hardware FP8 convert (exact, subnormals included).
+// MXFP4: the float whose exponent field is the E8M0 byte. The gfx950 scaled FP4 converts
+// apply only the exponent of their f32 scale operand, so this is exactly 2^(b-127) as far
+// as they are concerned (b = 0 gives 2^-127).
+template <int FMT>
+__device__ __forceinline__ void decode_scales(uint32_t w, float s[4]);
+template <>
+__device__ __forceinline__ void decode_scales<1>(uint32_t w, float s[4]) {
+  const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+  s[0] = lo[0];
+  s[1] = lo[1];
+  s[2] = hi[0];
+  s[3] = hi[1];
+}
+template <>
+__device__ __forceinline__ void decode_scales<2>(uint32_t w, float s[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = __uint_as_float(((w >> (8 * i)) & 0xFFu) << 23);
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 r;
@@ -66,13 +81,44 @@ __device__ __forceinline__ bf16x8 dq8_scaled(uint32_t q, float scale) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Dequantise one lane's share of a K-step: `q` holds 8 codes, `sbyte` the scale byte.
+// Dequantise one lane's share of a K-step to bf16: `q` holds 8 codes, `scale` comes from
+// decode_scales.
 template <int FMT>
-__device__ __forceinline__ bf16x8 dq8(uint32_t q, uint32_t sbyte);
+__device__ __forceinline__ bf16x8 dq8(uint32_t q, float scale);
 template <>
-__device__ __forceinline__ bf16x8 dq8<1>(uint32_t q, uint32_t sbyte) { return dq8_scaled(q, e4m3_to_f32(sbyte)); }
+__device__ __forceinline__ bf16x8 dq8<1>(uint32_t q, float scale) { return dq8_scaled(q, scale); }
 template <>
-__device__ __forceinline__ bf16x8 dq8<2>(uint32_t q, uint32_t sbyte) { return dq8_pow2(q, e8m0_as_scale(sbyte)); }
+__device__ __forceinline__ bf16x8 dq8<2>(uint32_t q, float scale) { return dq8_pow2(q, scale); }
+
+// NVFP4 to f16: an E4M3 scale s = 2^e * m with m in [1, 2) (sign kept with m). The scaled
+// convert applies 2^e; one packed f16 multiply applies m. Every E2M1 x E4M3 product lies in
+// [2^-10, 2880] with at most 6 significant bits, so the f16 result is exact -- at half the
+// VALU work of the f32 route.
+struct NvScaleF16 {
+  float pow2;
+  f16x2 mant;
+};
+__device__ __forceinline__ NvScaleF16 split_nv_scale(float s) {
+  const uint32_t b = __float_as_uint(s);
+  NvScaleF16 r;
+  r.pow2 = __uint_as_float(b & 0x7F800000u);
+  const _Float16 m = (_Float16)__uint_as_float((b & 0x807FFFFFu) | 0x3F800000u);
+  r.mant = f16x2{m, m};
+  return r;
+}
+__device__ __forceinline__ f16x8 dq8_nv_f16(uint32_t q, const NvScaleF16& sc) {
+  f16x2 v[4];
+  v[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc.pow2, 0) * sc.mant;
+  v[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc.pow2, 1) * sc.mant;
+  v[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc.pow2, 2) * sc.mant;
+  v[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc.pow2, 3) * sc.mant;
+  return __builtin_bit_cast(f16x8, v);
+}
+
+__device__ __forceinline__ f16x8 zero_f16x8() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(f16x8, z);
+}
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {
   u32x4 z = {0u, 0u, 0u, 0u};
@@ -95,7 +141,7 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ float silu_f32(float z) {
   // z * sigmoid(z) with the hardware exp2 and reciprocal; the oracle uses exact exp and the
   // bf16 tolerance absorbs the few-ulp difference.
-  return z * __frcp_rn(1.0f + __expf(-z));
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
 }  // namespace moe

@@ -34,43 +34,43 @@ constexpr int kLdsBuf = kTileRows * kLdsStride;         // bf16 per buffer
 constexpr int kStageChunks = kTileRows * (kKBlock / 8) / kGemmThreads;   // 16-byte chunks per thread: 8
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ uint32_t scale_dword(const uint8_t* sc_group, int64_t kb, int lane, bool nv) {
-  const int r = lane & 15;
-  const int64_t chunk = kb >> 2;
-  const int sub = int(kb & 3);
-  const int64_t off = nv ? chunk * 512 + ((lane >> 5) * 16 + r) * 16 + sub * 4 : chunk * 256 + r * 16 + sub * 4;
-  return *reinterpret_cast<const uint32_t*>(sc_group + off);
-}
+
+struct WRegs {
+  u32x4 q[4];                        // one 1 KiB fragment block per row group
+  uint32_t s[4];                     // its scale dword
+};
 
 template <int FMT, int PHASE>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
   extern __shared__ __align__(16) uint16_t lds[];
   const PreparedGeom& g = p.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool nv = FMT == FMT_NVFP4;
-  const int64_t n_mt = p.live[4];
-  const int64_t groups = PHASE == 1 ? g.n1_groups : g.n2_groups;
-  const int64_t n_nt = (groups + 15) / 16;
-  const int64_t kbs = PHASE == 1 ? g.kb1 : g.kb2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_mt = p.live[4];
+  const int groups = int(PHASE == 1 ? g.n1_groups : g.n2_groups);
+  const int n_nt = (groups + 15) / 16;
+  const int kbs = int(PHASE == 1 ? g.kb1 : g.kb2);
   const uint8_t* nib = PHASE == 1 ? p.nib1 : p.nib2;
   const uint8_t* scb = PHASE == 1 ? p.sc1 : p.sc2;
   const int64_t sc_per_group = PHASE == 1 ? g.sc1_per_group : g.sc2_per_group;
-  const int64_t n_items = n_mt * n_nt;
-  // Contiguous item ranges per XCD (workgroups are dealt to the XCDs round robin) so that
-  // the M tiles sharing one expert's N tile meet in the same L2.
-  const int64_t xcd = blockIdx.x % kXcds, wg_in_xcd = blockIdx.x / kXcds, wgs_per_xcd = gridDim.x / kXcds;
-  const int64_t per_xcd = (n_items + kXcds - 1) / kXcds;
-  const int64_t item_lo = xcd * per_xcd;
-  const int64_t item_hi = min(n_items, item_lo + per_xcd);
+  const int n_items = n_mt * n_nt;
+  // Items run M tile by M tile (N fastest) in contiguous ranges per XCD (workgroups are dealt
+  // to the XCDs round robin): the workgroups of one XCD share an activation tile in their L2,
+  // and the M tiles of one expert revisit its weight tiles while they are still in the
+  // Infinity Cache.
+  const int xcd = blockIdx.x % kXcds, wg_in_xcd = blockIdx.x / kXcds, wgs_per_xcd = gridDim.x / kXcds;
+  const int per_xcd = (n_items + kXcds - 1) / kXcds;
+  const int item_lo = xcd * per_xcd;
+  const int item_hi = min(n_items, item_lo + per_xcd);
   const int seg = tid & 15;              // staging: this thread's 16-byte column segment
   const int srow0 = tid >> 4;            // and its first row (rows srow0 + 16 j)
+  const int sc_lane = FMT == FMT_NVFP4 ? ((lane >> 5) * 16 + (lane & 15)) * 16 : (lane & 15) * 16;
 
-  for (int64_t item = item_lo + wg_in_xcd; item < item_hi; item += wgs_per_xcd) {
-    const int64_t nt = item / n_mt, mt = item % n_mt;
+  for (int item = item_lo + wg_in_xcd; item < item_hi; item += wgs_per_xcd) {
+    const int mt = item / n_nt, nt = item % n_nt;
     const int2 tile = p.tiles[mt];
     const int64_t fb = tile.x;
     const int nb = tile.y & 0xFF;
-    const int e = tile.y >> 8;
+    const int e = __builtin_amdgcn_readfirstlane(tile.y >> 8);
     const int rows = nb * kBlockM;
 
     // Source offsets (in bf16 elements, at K block 0) of this thread's staging rows; -1 = zero row.
@@ -91,10 +91,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
     }
     const uint16_t* bsrc = PHASE == 1 ? p.x : p.inter;
     const int64_t kmax = PHASE == 1 ? g.H : g.ip;
-    auto stage_load = [&](int64_t kb, u32x4* r) {
+    auto stage_load = [&](int kb, u32x4* r) {
 #pragma unroll
       for (int j = 0; j < kStageChunks; ++j) {
-        const int64_t k = kb * kKBlock;
+        const int64_t k = int64_t(kb) * kKBlock;
         if (src[j] >= 0 && k + seg * 8 < kmax) r[j] = *reinterpret_cast<const u32x4*>(bsrc + src[j] + k);
         else r[j] = u32x4{0u, 0u, 0u, 0u};
       }
@@ -107,26 +107,27 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
       }
     };
 
-    // This wave's four row groups.
-    const int64_t rg_base = nt * 16 + wave * 4;
+    // This wave's four row groups (wave-uniform base addresses; lanes add 32-bit offsets).
+    const int rg_base = nt * 16 + wave * 4;
+    bool fvalid[4];
     const uint8_t* nbp[4];
     const uint8_t* sgp[4];
-    bool fvalid[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const int64_t rg = rg_base + f;
+      const int rg = rg_base + f;
       fvalid[f] = rg < groups;
-      const int64_t rgc = fvalid[f] ? rg : 0;
-      nbp[f] = nib + ((int64_t(e) * groups + rgc) * kbs) * kFragBytes + lane * 16;
-      sgp[f] = scb + (int64_t(e) * groups + rgc) * sc_per_group;
+      const int64_t gi = int64_t(e) * groups + (fvalid[f] ? rg : 0);
+      nbp[f] = nib + gi * kbs * kFragBytes;
+      sgp[f] = scb + gi * sc_per_group;
     }
-    auto load_w = [&](int64_t kb, u32x4* q, uint32_t* s) {
+    // Loads are unconditional (a K block past the end re-reads the last one, never used) so
+    // the wait counters stay exact across the three-deep ring below.
+    auto load_w = [&](int kb, WRegs& w) {
+      kb = min(kb, kbs - 1);
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        if (fvalid[f]) {
-          q[f] = *reinterpret_cast<const u32x4*>(nbp[f] + kb * kFragBytes);
-          s[f] = scale_dword(sgp[f], kb, lane, nv);
-        }
+        w.q[f] = *reinterpret_cast<const u32x4*>(nbp[f] + int64_t(kb) * kFragBytes + lane * 16);
+        w.s[f] = *reinterpret_cast<const uint32_t*>(sgp[f] + int64_t(kb >> 2) * g.sc_chunk_bytes + sc_lane + (kb & 3) * 4);
       }
     };
 
@@ -136,25 +137,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
 #pragma unroll
       for (int b = 0; b < kTileBlocks; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 xr[kStageChunks];
-    u32x4 qc[4], qn[4];
-    uint32_t sc[4], sn[4];
-    stage_load(0, xr);
-    load_w(0, qc, sc);
-    stage_store(0, xr);
-    __syncthreads();
-    for (int64_t kb = 0; kb < kbs; ++kb) {
-      const bool more = kb + 1 < kbs;
-      if (more) {
-        stage_load(kb + 1, xr);
-        load_w(kb + 1, qn, sn);
-      }
-      const uint16_t* buf = lds + (kb & 1) * kLdsBuf;
+    auto compute = [&](int buf_idx, const WRegs& w) {
+      const uint16_t* buf = lds + buf_idx * kLdsBuf;
+      float scl[4][4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) decode_scales<FMT>(w.s[f], scl[f]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         bf16x8 a[4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) a[f] = fvalid[f] ? dq8<FMT>(qc[f][s], (sc[f] >> (8 * s)) & 0xFF) : zero_bf16x8();
+        for (int f = 0; f < 4; ++f) a[f] = dq8<FMT>(w.q[f][s], scl[f][s]);
 #pragma unroll
         for (int b = 0; b < kTileBlocks; ++b) {
           if (b < nb) {
@@ -165,13 +157,32 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
           }
         }
       }
-      if (more) stage_store((kb + 1) & 1, xr);
-      __syncthreads();
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        qc[f] = qn[f];
-        sc[f] = sn[f];
+    };
+
+    // One K block per step: weights two blocks ahead in registers, activations one block
+    // ahead in the other LDS buffer; barriers order LDS only, so the weight loads in flight
+    // are not drained.
+    u32x4 xr[kStageChunks];
+    auto step = [&](int kb, const WRegs& cur, WRegs& ahead2) {
+      if (kb < kbs) {
+        load_w(kb + 2, ahead2);
+        const bool more = kb + 1 < kbs;
+        if (more) stage_load(kb + 1, xr);
+        compute(kb & 1, cur);
+        if (more) stage_store((kb + 1) & 1, xr);
       }
+      lds_barrier();
+    };
+    WRegs wa, wb, wc;
+    stage_load(0, xr);
+    load_w(0, wa);
+    load_w(1, wb);
+    stage_store(0, xr);
+    lds_barrier();
+    for (int kb = 0; kb < kbs; kb += 3) {
+      step(kb, wa, wc);
+      step(kb + 1, wb, wa);
+      step(kb + 2, wc, wb);
     }
 
     // Epilogue.
@@ -193,7 +204,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                   a[i] = silu_f32(acc[2 * pr][b][i] * g13) * (acc[2 * pr + 1][b][i] * g13) * rw;
-                const int64_t icol = ((rg_base + 2 * pr) >> 1) * 16 + r0;
+                const int64_t icol = int64_t((rg_base + 2 * pr) >> 1) * 16 + r0;
                 *reinterpret_cast<uint2*>(dst + icol) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
               }
             }
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
                   const float u = fmaxf(acc[f][b][i] * g13, 0.f);
                   a[i] = u * u * rw;
                 }
-                const int64_t icol = (rg_base + f) * 16 + r0;
+                const int64_t icol = int64_t(rg_base + f) * 16 + r0;
                 *reinterpret_cast<uint2*>(dst + icol) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
               }
             }
@@ -224,7 +235,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
               if (fvalid[f]) {
-                const int64_t h = (rg_base + f) * 16 + r0;
+                const int64_t h = int64_t(rg_base + f) * 16 + r0;
                 float* dst = p.acc + int64_t(t) * g.H + h;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
