@@ -7,6 +7,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <cstdint>
 #include <string>
 
 #include "../../include/moe_w4a16.h"
@@ -266,6 +267,10 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   if (decode && token_capacity > kDecodeMaxM)
     return fail(MOE_ERR_UNSUPPORTED, "decode path needs token_capacity <= %d (got %lld)", kDecodeMaxM,
                 (long long)token_capacity);
+  // The grouped GEMM addresses activation and intermediate rows with 32-bit buffer offsets.
+  if (!decode && (m * int64_t(dims->hidden) * 2 > INT32_MAX - 4096 ||
+                  fg.pack.cap_routes * g.ip * 2 > INT32_MAX - 4096))
+    return fail(MOE_ERR_UNSUPPORTED, "grouped GEMM: m x hidden or the intermediate rows exceed 2 GiB");
   int cus = 0;
   if (int rc = check_device(&cus)) return rc;
   if (m == 0) return ok();

@@ -28,224 +28,313 @@ namespace moe {
 namespace {
 
 constexpr int kGemmThreads = 256;
-constexpr int kTileRows = kTileBlocks * kBlockM;        // 128
-constexpr int kLdsStride = kKBlock + 8;                 // bf16 per LDS row (16 B pad vs bank conflicts)
-constexpr int kLdsBuf = kTileRows * kLdsStride;         // bf16 per buffer
-constexpr int kStageChunks = kTileRows * (kKBlock / 8) / kGemmThreads;   // 16-byte chunks per thread: 8
-constexpr int kXcds = 8;
+constexpr uint32_t kOutOfRange = 0x80000000u;           // set in a buffer offset: past every num_records, loads 0
+constexpr int kRowBytes = kKBlock * 2;                  // one activation row of a K block: 256 B
+constexpr int kWaveW = 4 * kFragBytes;                  // one wave's four fragment blocks of a K block
+constexpr int kLdsBytes = 147456;                       // the pipeline ring (144 KiB of the 160 KiB LDS)
 
-
-struct WRegs {
-  u32x4 q[4];                        // one 1 KiB fragment block per row group
-  uint32_t s[4];                     // its scale dword
+// Ring of K-block stages in LDS, filled by buffer loads that write LDS directly (no register
+// staging): an activation tile of 16 NB rows x 256 B, then each wave's 4 fragment blocks.
+template <int NB>
+struct Ring {
+  static constexpr int kStage = NB * kBlockM * kRowBytes + 4 * kWaveW;
+  static constexpr int kDepth = kLdsBytes / kStage;                  // 3 (NB 8) .. 7 (NB 1)
+  static constexpr int kLoads = NB + 4 + 4;                          // vector loads a wave issues per stage
 };
+
+// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14; expcnt and lgkmcnt at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier for the stage ring. A release fence would make every wave wait for all of
+// its loads into LDS, including the stages still meant to be in flight; instead each wave
+// waits explicitly for the stage it needs (wait_vmcnt) and for its own LDS reads (lgkmcnt 0,
+// so the slot about to be refilled is no longer being read), then meets the others. The
+// acquire fence keeps later LDS reads below the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// A pointer the compiler cannot prove wave-uniform, moved to scalar registers (it is uniform).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const uint8_t* lds_dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, int(voff), 0, 0, 0);
+}
+
+// Per-launch constants shared by every item of a workgroup.
+struct GemmCtx {
+  int groups, kbs;
+  int64_t sc_per_group;
+  const uint8_t* nib;
+  const uint8_t* scb;
+  __amdgpu_buffer_rsrc_t act;        // x (FC1) or the intermediate rows (FC2), bounds-checked
+  int act_row_bytes, k_bytes;        // row pitch of that buffer and its K extent, in bytes
+};
+
+// One item: NB route blocks (16 NB rows) of one expert x 256 weight rows (16 row groups,
+// 4 per wave), full K.
+template <int FMT, int PHASE, int NB>
+__device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c, uint8_t* lds, int mt, int nt) {
+  using R = Ring<NB>;
+  constexpr int D = R::kDepth;
+  const PreparedGeom& g = p.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int2 tile = p.tiles[mt];
+  const int64_t fb = tile.x;
+  const int nb = __builtin_amdgcn_readfirstlane(tile.y & 0xFF);
+  const int e = __builtin_amdgcn_readfirstlane(tile.y >> 8);
+  const int kbs = c.kbs;
+
+  // Activation rows. Load j of wave w fills tile rows 4q .. 4q+3 (q = w NB + j), lane l the
+  // 16-byte chunk position l % 16 of row 4q + l / 16 with the row's chunk (l % 16) ^ (row % 16):
+  // the XOR swizzle lets the 16 lanes that read one chunk column of 16 rows hit 16 distinct
+  // bank groups. Padding slots and blocks past the tile read 0 through the bounds check.
+  uint32_t src[NB], chunk[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int row = 4 * (wave * NB + j) + (lane >> 4);
+    const int64_t slot = fb * kBlockM + row;
+    const int t = row < nb * kBlockM ? p.slot_info[slot].x : -1;
+    const int64_t src_row = PHASE == 1 ? int64_t(t) : slot;   // x row of the token, or the slot's own row
+    chunk[j] = uint32_t((lane & 15) ^ (row & 15)) << 4;
+    src[j] = t >= 0 ? uint32_t(src_row * c.act_row_bytes) + chunk[j] : kOutOfRange;
+  }
+  // This wave's four row groups are contiguous in the prepared buffer; groups past the end
+  // (last N tile only) fall outside the resource and read 0.
+  const int rg_base = nt * 16 + wave * 4;
+  const int live_groups = max(0, min(4, c.groups - rg_base));
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(c.nib + (int64_t(e) * c.groups + min(rg_base, c.groups - 1)) * kbs * kFragBytes), 0,
+      __builtin_amdgcn_readfirstlane(live_groups * kbs * kFragBytes), 0x00020000);
+  const uint8_t* sgp[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int rg = min(rg_base + f, c.groups - 1);
+    sgp[f] = c.scb + (int64_t(e) * c.groups + rg) * c.sc_per_group;
+  }
+  const int sc_lane = FMT == FMT_NVFP4 ? ((lane >> 5) * 16 + (lane & 15)) * 16 : (lane & 15) * 16;
+
+  // One stage: the activation K block and this wave's weight K block into LDS slot `slot`, its
+  // scale dwords into registers. Blocks past K are clamped (weights) or read 0 (activations):
+  // every stage issues the same R::kLoads loads, so the vmcnt arithmetic below is exact.
+  uint32_t sc[D][4];
+  auto issue = [&](int kb, int slot, uint32_t* scd) {
+    uint8_t* st = lds + slot * R::kStage;
+    const uint32_t k = uint32_t(kb) * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      dma16(c.act, st + (wave * NB + j) * 1024, (src[j] + k) | (k + chunk[j] < uint32_t(c.k_bytes) ? 0u : kOutOfRange));
+    const int kc = min(kb, kbs - 1);
+    uint8_t* wst = st + NB * kBlockM * kRowBytes + wave * kWaveW;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) dma16(wres, wst + f * kFragBytes, uint32_t((f * kbs + kc) * kFragBytes + lane * 16));
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      scd[f] = *reinterpret_cast<const uint32_t*>(sgp[f] + int64_t(kc >> 2) * g.sc_chunk_bytes + sc_lane + (kc & 3) * 4);
+  };
+
+  f32x4 acc[4][NB];
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One K block: four MFMA K-steps. The activation reads and dequantisation of step s+1 are
+  // issued ahead of the MFMAs of step s, and the scheduler is asked to interleave them one
+  // MFMA at a time so the matrix pipe stays busy while LDS and the VALU work.
+  constexpr int kDqValu = FMT == FMT_NVFP4 ? 16 : 4;           // VALU ops of one dq8
+  constexpr int kValuPerMfma = (4 * kDqValu + 4 * NB - 1) / (4 * NB);
+  auto compute = [&](int slot, const uint32_t* scd) {
+    const uint8_t* st = lds + slot * R::kStage;
+    const uint8_t* xrow = st + (lane & 15) * kRowBytes;
+    const int sw = lane & 15;
+    u32x4 wq[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      wq[f] = *reinterpret_cast<const u32x4*>(st + NB * kBlockM * kRowBytes + wave * kWaveW + f * kFragBytes + lane * 16);
+    float scl[4][4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) decode_scales<FMT>(scd[f], scl[f]);
+    auto xread = [&](int b, int s) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+          xrow + b * kBlockM * kRowBytes + (((4 * s + (lane >> 4)) ^ sw) << 4)));
+    };
+    bf16x8 xb[2][NB], a[2][4];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) xb[0][b] = xread(b, 0);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) a[0][f] = dq8<FMT>(wq[f][0], scl[f][0]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int cur = s & 1, nxt = cur ^ 1;
+      if (s < 3) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) xb[nxt][b] = xread(b, s + 1);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) a[nxt][f] = dq8<FMT>(wq[f][s + 1], scl[f][s + 1]);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) acc[f][b] = mfma16(a[cur][f], xb[cur][b], acc[f][b]);
+      if (s < 3) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // one LDS read
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);    // dequant VALU
+          }
+        }
+      }
+    }
+  };
+
+  // Pipeline: stages 0 .. D-2 in flight before the loop; step kb waits until its own stage has
+  // landed (at most D-2 later stages still outstanding), meets the other waves at a barrier
+  // (their loads have landed too, and all are done with slot (kb-1) % D), refills that slot
+  // with stage kb+D-1 and computes stage kb. Barriers order LDS only.
+  auto step = [&](int kb, int j) {
+    wait_vmcnt<(D - 2) * R::kLoads>();
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kb + D - 1, (j + D - 1) % D, sc[(j + D - 1) % D]);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(j, sc[j]);
+  };
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) issue(j, j, sc[j]);
+  __builtin_amdgcn_sched_barrier(0);
+  int kb = 0;
+  for (; kb + D <= kbs; kb += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) step(kb + j, j);
+  }
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j)
+    if (kb + j < kbs) step(kb + j, j);
+  // Drain the stages issued past K before the slots are reused by the next item.
+  wait_vmcnt<0>();
+
+  // Epilogue. Lane (r0 = 4 (lane / 16), col = lane % 16) holds rows r0..r0+3 of each
+  // 16-row group, route column col of each block.
+  const int r0 = 4 * (lane >> 4), col = lane & 15;
+  if (PHASE == 1) {
+    const float g13 = p.g13[e], g2 = p.g2[e];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b < nb) {
+        const int64_t slot = (fb + b) * kBlockM + col;
+        const int2 info = p.slot_info[slot];
+        const float rw = info.x >= 0 ? __int_as_float(info.y) * g2 : 0.f;
+        uint16_t* dst = p.inter + slot * g.ip;
+        if (g.act == ACT_SWIGLU) {
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            if (rg_base + 2 * pr < c.groups) {
+              float a[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                a[i] = silu_f32(acc[2 * pr][b][i] * g13) * (acc[2 * pr + 1][b][i] * g13) * rw;
+              const int64_t icol = int64_t((rg_base + 2 * pr) >> 1) * 16 + r0;
+              *reinterpret_cast<uint2*>(dst + icol) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            if (rg_base + f < c.groups) {
+              float a[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float u = fmaxf(acc[f][b][i] * g13, 0.f);
+                a[i] = u * u * rw;
+              }
+              const int64_t icol = int64_t(rg_base + f) * 16 + r0;
+              *reinterpret_cast<uint2*>(dst + icol) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+            }
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b < nb) {
+        const int64_t slot = (fb + b) * kBlockM + col;
+        const int t = p.slot_info[slot].x;
+        if (t >= 0) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            if (rg_base + f < c.groups) {
+              const int64_t h = int64_t(rg_base + f) * 16 + r0;
+              float* dst = p.acc + int64_t(t) * g.H + h;
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (h + i < g.H) atomicAdd(dst + i, acc[f][b][i]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
 
 template <int FMT, int PHASE>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
-  extern __shared__ __align__(16) uint16_t lds[];
+  extern __shared__ __align__(16) uint8_t lds[];
   const PreparedGeom& g = p.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  GemmCtx c;
+  c.groups = int(PHASE == 1 ? g.n1_groups : g.n2_groups);
+  c.kbs = int(PHASE == 1 ? g.kb1 : g.kb2);
+  c.nib = PHASE == 1 ? p.nib1 : p.nib2;
+  c.scb = PHASE == 1 ? p.sc1 : p.sc2;
+  c.sc_per_group = PHASE == 1 ? g.sc1_per_group : g.sc2_per_group;
+  if (PHASE == 1) {
+    c.act_row_bytes = g.H * 2;
+    c.k_bytes = g.H * 2;
+    c.act = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x), 0, int(int64_t(p.m) * g.H * 2), 0x00020000);
+  } else {
+    c.act_row_bytes = int(g.ip * 2);
+    c.k_bytes = int(g.ip * 2);
+    c.act = __builtin_amdgcn_make_buffer_rsrc(p.inter, 0, int(p.cap_blocks * kBlockM * g.ip * 2), 0x00020000);
+  }
   const int n_mt = p.live[4];
-  const int groups = int(PHASE == 1 ? g.n1_groups : g.n2_groups);
-  const int n_nt = (groups + 15) / 16;
-  const int kbs = int(PHASE == 1 ? g.kb1 : g.kb2);
-  const uint8_t* nib = PHASE == 1 ? p.nib1 : p.nib2;
-  const uint8_t* scb = PHASE == 1 ? p.sc1 : p.sc2;
-  const int64_t sc_per_group = PHASE == 1 ? g.sc1_per_group : g.sc2_per_group;
+  const int n_nt = (c.groups + 15) / 16;
   const int n_items = n_mt * n_nt;
-  // Items run M tile by M tile (N fastest) in contiguous ranges per XCD (workgroups are dealt
-  // to the XCDs round robin): the workgroups of one XCD share an activation tile in their L2,
-  // and the M tiles of one expert revisit its weight tiles while they are still in the
-  // Infinity Cache.
-  const int xcd = blockIdx.x % kXcds, wg_in_xcd = blockIdx.x / kXcds, wgs_per_xcd = gridDim.x / kXcds;
-  const int per_xcd = (n_items + kXcds - 1) / kXcds;
-  const int item_lo = xcd * per_xcd;
-  const int item_hi = min(n_items, item_lo + per_xcd);
-  const int seg = tid & 15;              // staging: this thread's 16-byte column segment
-  const int srow0 = tid >> 4;            // and its first row (rows srow0 + 16 j)
-  const int sc_lane = FMT == FMT_NVFP4 ? ((lane >> 5) * 16 + (lane & 15)) * 16 : (lane & 15) * 16;
-
-  for (int item = item_lo + wg_in_xcd; item < item_hi; item += wgs_per_xcd) {
-    const int mt = item / n_nt, nt = item % n_nt;
-    const int2 tile = p.tiles[mt];
-    const int64_t fb = tile.x;
-    const int nb = tile.y & 0xFF;
-    const int e = __builtin_amdgcn_readfirstlane(tile.y >> 8);
-    const int rows = nb * kBlockM;
-
-    // Source offsets (in bf16 elements, at K block 0) of this thread's staging rows; -1 = zero row.
-    int64_t src[kStageChunks];
-#pragma unroll
-    for (int j = 0; j < kStageChunks; ++j) {
-      const int row = srow0 + 16 * j;
-      src[j] = -1;
-      if (row < rows) {
-        const int64_t slot = fb * kBlockM + row;
-        if (PHASE == 1) {
-          const int t = p.slot_info[slot].x;
-          if (t >= 0) src[j] = int64_t(t) * g.H + seg * 8;
-        } else {
-          src[j] = slot * g.ip + seg * 8;
-        }
-      }
-    }
-    const uint16_t* bsrc = PHASE == 1 ? p.x : p.inter;
-    const int64_t kmax = PHASE == 1 ? g.H : g.ip;
-    auto stage_load = [&](int kb, u32x4* r) {
-#pragma unroll
-      for (int j = 0; j < kStageChunks; ++j) {
-        const int64_t k = int64_t(kb) * kKBlock;
-        if (src[j] >= 0 && k + seg * 8 < kmax) r[j] = *reinterpret_cast<const u32x4*>(bsrc + src[j] + k);
-        else r[j] = u32x4{0u, 0u, 0u, 0u};
-      }
-    };
-    auto stage_store = [&](int buf, const u32x4* r) {
-#pragma unroll
-      for (int j = 0; j < kStageChunks; ++j) {
-        const int row = srow0 + 16 * j;
-        if (row < rows) *reinterpret_cast<u32x4*>(lds + buf * kLdsBuf + row * kLdsStride + seg * 8) = r[j];
-      }
-    };
-
-    // This wave's four row groups (wave-uniform base addresses; lanes add 32-bit offsets).
-    const int rg_base = nt * 16 + wave * 4;
-    bool fvalid[4];
-    const uint8_t* nbp[4];
-    const uint8_t* sgp[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int rg = rg_base + f;
-      fvalid[f] = rg < groups;
-      const int64_t gi = int64_t(e) * groups + (fvalid[f] ? rg : 0);
-      nbp[f] = nib + gi * kbs * kFragBytes;
-      sgp[f] = scb + gi * sc_per_group;
-    }
-    // Loads are unconditional (a K block past the end re-reads the last one, never used) so
-    // the wait counters stay exact across the three-deep ring below.
-    auto load_w = [&](int kb, WRegs& w) {
-      kb = min(kb, kbs - 1);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        w.q[f] = *reinterpret_cast<const u32x4*>(nbp[f] + int64_t(kb) * kFragBytes + lane * 16);
-        w.s[f] = *reinterpret_cast<const uint32_t*>(sgp[f] + int64_t(kb >> 2) * g.sc_chunk_bytes + sc_lane + (kb & 3) * 4);
-      }
-    };
-
-    f32x4 acc[4][kTileBlocks];
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-#pragma unroll
-      for (int b = 0; b < kTileBlocks; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto compute = [&](int buf_idx, const WRegs& w) {
-      const uint16_t* buf = lds + buf_idx * kLdsBuf;
-      float scl[4][4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) decode_scales<FMT>(w.s[f], scl[f]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 a[4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) a[f] = dq8<FMT>(w.q[f][s], scl[f][s]);
-#pragma unroll
-        for (int b = 0; b < kTileBlocks; ++b) {
-          if (b < nb) {
-            const bf16x8 xb = load_bf16x8(buf + (b * kBlockM + (lane & 15)) * kLdsStride + 32 * s + 8 * (lane >> 4));
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-              if (fvalid[f]) acc[f][b] = mfma16(a[f], xb, acc[f][b]);
-          }
-        }
-      }
-    };
-
-    // One K block per step: weights two blocks ahead in registers, activations one block
-    // ahead in the other LDS buffer; barriers order LDS only, so the weight loads in flight
-    // are not drained.
-    u32x4 xr[kStageChunks];
-    auto step = [&](int kb, const WRegs& cur, WRegs& ahead2) {
-      if (kb < kbs) {
-        load_w(kb + 2, ahead2);
-        const bool more = kb + 1 < kbs;
-        if (more) stage_load(kb + 1, xr);
-        compute(kb & 1, cur);
-        if (more) stage_store((kb + 1) & 1, xr);
-      }
-      lds_barrier();
-    };
-    WRegs wa, wb, wc;
-    stage_load(0, xr);
-    load_w(0, wa);
-    load_w(1, wb);
-    stage_store(0, xr);
+  // Persistent workgroups take items from a queue (reset by the route packer) in M-tile
+  // order, N fastest: the workgroups that share an activation tile, and the consecutive M
+  // tiles of one expert that share its weight tiles, run at the same time, so the re-reads
+  // hit the caches; full tiles are queued first, so the load stays balanced to the end.
+  __shared__ int s_item;
+  int* queue = p.live + (PHASE == 1 ? 5 : 6);
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(queue, 1);
     lds_barrier();
-    for (int kb = 0; kb < kbs; kb += 3) {
-      step(kb, wa, wc);
-      step(kb + 1, wb, wa);
-      step(kb + 2, wc, wb);
-    }
-
-    // Epilogue.
-    const int r0 = 4 * (lane >> 4), col = lane & 15;
-    if (PHASE == 1) {
-      const float g13 = p.g13[e], g2 = p.g2[e];
-#pragma unroll
-      for (int b = 0; b < kTileBlocks; ++b) {
-        if (b < nb) {
-          const int64_t slot = (fb + b) * kBlockM + col;
-          const int2 info = p.slot_info[slot];
-          const float rw = info.x >= 0 ? __int_as_float(info.y) * g2 : 0.f;
-          uint16_t* dst = p.inter + slot * g.ip;
-          if (g.act == ACT_SWIGLU) {
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-              if (fvalid[2 * pr]) {
-                float a[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  a[i] = silu_f32(acc[2 * pr][b][i] * g13) * (acc[2 * pr + 1][b][i] * g13) * rw;
-                const int64_t icol = int64_t((rg_base + 2 * pr) >> 1) * 16 + r0;
-                *reinterpret_cast<uint2*>(dst + icol) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-              }
-            }
-          } else {
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-              if (fvalid[f]) {
-                float a[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const float u = fmaxf(acc[f][b][i] * g13, 0.f);
-                  a[i] = u * u * rw;
-                }
-                const int64_t icol = int64_t(rg_base + f) * 16 + r0;
-                *reinterpret_cast<uint2*>(dst + icol) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-              }
-            }
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < kTileBlocks; ++b) {
-        if (b < nb) {
-          const int64_t slot = (fb + b) * kBlockM + col;
-          const int t = p.slot_info[slot].x;
-          if (t >= 0) {
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-              if (fvalid[f]) {
-                const int64_t h = int64_t(rg_base + f) * 16 + r0;
-                float* dst = p.acc + int64_t(t) * g.H + h;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  if (h + i < g.H) atomicAdd(dst + i, acc[f][b][i]);
-              }
-            }
-          }
-        }
-      }
-    }
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item >= n_items) break;
+    // Every item starts with a barrier after this read, so thread 0 cannot overwrite
+    // s_item before all threads have taken it.
+    const int mt = item / n_nt, nt = item % n_nt;
+    const int nb = __builtin_amdgcn_readfirstlane(p.tiles[mt].y & 0xFF);
+    // Tiles are compiled for 1, 2, 4 or 8 route blocks so that the MFMA loop is straight-line.
+    if (nb <= 1) gemm_item<FMT, PHASE, 1>(p, c, lds, mt, nt);
+    else if (nb <= 2) gemm_item<FMT, PHASE, 2>(p, c, lds, mt, nt);
+    else if (nb <= 4) gemm_item<FMT, PHASE, 4>(p, c, lds, mt, nt);
+    else gemm_item<FMT, PHASE, 8>(p, c, lds, mt, nt);
   }
 }
 
@@ -267,7 +356,7 @@ __global__ void finalize_kernel(const float* __restrict__ acc, uint16_t* __restr
 
 template <int FMT, int PHASE>
 hipError_t allow_large_lds(size_t lds) {
-  // The double-buffered tile needs more than the 64 KiB default of dynamic LDS.
+  // The stage ring needs more than the 64 KiB default of dynamic LDS.
   static hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<FMT, PHASE>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   return once;
@@ -275,8 +364,8 @@ hipError_t allow_large_lds(size_t lds) {
 
 hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks) {
   // One 4-wave workgroup per CU: 128 accumulator AGPRs + ~230 VGPRs per wave leave room for one.
-  const int grid = ((num_cus + kXcds - 1) / kXcds) * kXcds;
-  const size_t lds = size_t(2) * kLdsBuf * sizeof(uint16_t);
+  const int grid = num_cus;
+  const size_t lds = kLdsBytes;
   hipError_t e = p.g.fmt == FMT_NVFP4 ? allow_large_lds<FMT_NVFP4, 1>(lds) : allow_large_lds<FMT_MXFP4, 1>(lds);
   if (e == hipSuccess) e = p.g.fmt == FMT_NVFP4 ? allow_large_lds<FMT_NVFP4, 2>(lds) : allow_large_lds<FMT_MXFP4, 2>(lds);
   if (e != hipSuccess) return e;

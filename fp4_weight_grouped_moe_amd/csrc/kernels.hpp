@@ -18,7 +18,7 @@ struct RoutePackParams {
   int32_t* expert_offsets;
   int32_t* sorted_route_ids;
   int32_t* block_expert;
-  int32_t* live;                 // [8]: valid, padded, live blocks, m, M tiles
+  int32_t* live;                 // [8]: valid, padded, live blocks, m, M tiles, two queue counters
   int32_t* route_slot;
   int2* tiles;                   // [cap_blocks] (first block, blocks | expert << 8) or null
   int2* slot_info;               // [cap_routes] (token, router weight bits) or null
@@ -54,7 +54,7 @@ struct FusedParams {
   int32_t topk;
   const int32_t* sorted_route_ids;
   const int32_t* block_expert;
-  const int32_t* live;
+  int32_t* live;                 // route-pack counts; [5], [6] = grouped-GEMM work queues
   const int2* tiles;
   const int2* slot_info;
   const int32_t* route_slot;      // [m * topk] packed slot of each route or -1

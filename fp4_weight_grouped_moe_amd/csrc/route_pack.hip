@@ -76,15 +76,17 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   __syncthreads();
 
   // Padded segment offsets and the M-tile table, kPackThreads experts per pass of the scan.
+  // Full tiles (kTileBlocks blocks) come first, then each expert's partial tail tile, so a
+  // queue that hands the tiles out in order starts the longest work first.
   int carry = 0, tile_carry = 0;
   for (int base = 0; base < E; base += kPackThreads) {
     int e = base + tid;
     int c = e < E ? cnt[e] : 0;
     int padded = (c + B - 1) / B * B;
-    int ntile = (padded / B + kTileBlocks - 1) / kTileBlocks;
+    int nfull = padded / B / kTileBlocks;
     int tot, ttot;
     int off = block_exclusive_scan(padded, wave_tot, &tot) + carry;
-    int toff = block_exclusive_scan(ntile, wave_tot, &ttot) + tile_carry;
+    int toff = block_exclusive_scan(nfull, wave_tot, &ttot) + tile_carry;
     if (e < E) {
       p.expert_counts[e] = c;
       p.expert_offsets[e] = off;
@@ -94,11 +96,8 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
         if (p.slot_info) p.slot_info[s] = make_int2(-1, 0);
       }
       if (p.tiles) {
-        for (int t = 0; t < ntile; ++t) {
-          int first = off / B + t * kTileBlocks;
-          int nb = min(kTileBlocks, (off + padded) / B - first);
-          p.tiles[toff + t] = make_int2(first, nb | (e << 8));
-        }
+        for (int t = 0; t < nfull; ++t)
+          p.tiles[toff + t] = make_int2(off / B + t * kTileBlocks, kTileBlocks | (e << 8));
       }
       cnt[e] = off;                                        // running slot of expert e
     }
@@ -106,12 +105,30 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
     tile_carry += ttot;
   }
   const int total_padded = carry;
+  if (p.tiles) {
+    // Partial tiles after all full ones. Thread e reads back the offsets it wrote above.
+    for (int base = 0; base < E; base += kPackThreads) {
+      int e = base + tid;
+      int blocks = 0, off = 0;
+      if (e < E) {
+        off = p.expert_offsets[e];
+        blocks = (p.expert_counts[e] + B - 1) / B;
+      }
+      int rem = blocks % kTileBlocks;
+      int ttot;
+      int toff = block_exclusive_scan(rem > 0 ? 1 : 0, wave_tot, &ttot) + tile_carry;
+      if (rem > 0) p.tiles[toff] = make_int2(off / B + blocks - rem, rem | (e << 8));
+      tile_carry += ttot;
+    }
+  }
   if (tid == 0) {
     p.expert_offsets[E] = total_padded;
     p.live[1] = total_padded;
     p.live[2] = total_padded / B;
     p.live[3] = int(p.m);
     p.live[4] = tile_carry;
+    p.live[5] = 0;                                         // grouped-GEMM work queues (FC1, FC2)
+    p.live[6] = 0;
   }
   for (int64_t s = total_padded + tid; s < p.cap_routes; s += kPackThreads) {
     p.sorted_route_ids[s] = -1;
