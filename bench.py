@@ -212,7 +212,7 @@ def main():
     for i in range(args.steps):
         step(args.warmup + i, [hev.ev[5 * i + j] for j in range(5)])
     torch.cuda.synchronize()
-    names = ["route_pack", "fc1", "fc2", "cast"]
+    names = ["route_pack", "fc1", "fc2", "combine"]
     per = {n: 0.0 for n in names}
     for i in range(args.steps):
         for j, n in enumerate(names):

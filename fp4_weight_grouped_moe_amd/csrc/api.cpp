@@ -180,10 +180,7 @@ int moe_route_pack(const int32_t* topk_ids, int64_t m, int topk, const int32_t* 
   rp.route_slot = reinterpret_cast<int32_t*>(ws + pg.off_route_slot);
   rp.tiles = nullptr;
   rp.slot_info = nullptr;
-  rp.acc = nullptr;
-  rp.acc_elems = 0;
-  rp.zero_ints = nullptr;
-  rp.n_zero_ints = 0;
+  rp.x16 = nullptr;
   out->expert_counts = rp.expert_counts;
   out->expert_offsets = rp.expert_offsets;
   out->sorted_route_ids = rp.sorted_route_ids;
@@ -299,10 +296,11 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   rp.route_slot = reinterpret_cast<int32_t*>(pk + pg.off_route_slot);
   rp.tiles = reinterpret_cast<int2*>(pk + pg.off_tiles);
   rp.slot_info = reinterpret_cast<int2*>(pk + pg.off_tok_of_slot);
-  rp.acc = decode ? nullptr : reinterpret_cast<float*>(ws + fg.off_acc);
-  rp.acc_elems = decode ? 0 : m * dims->hidden;
-  rp.zero_ints = decode ? reinterpret_cast<int32_t*>(ws + fg.off_arrivals) : nullptr;
-  rp.n_zero_ints = decode ? fg.n_arrivals : 0;
+  const bool convert = !decode && dims->fmt == MOE_FMT_NVFP4_E4M3_K16;
+  rp.x = x;
+  rp.x16 = convert ? reinterpret_cast<uint16_t*>(ws + fg.off_x16) : nullptr;
+  rp.xexp = convert ? reinterpret_cast<int32_t*>(ws + fg.off_xexp) : nullptr;
+  rp.hidden = dims->hidden;
 
   FusedParams fp{};
   const uint8_t* pw = static_cast<const uint8_t*>(prepared);
@@ -324,9 +322,9 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   fp.slot_info = rp.slot_info;
   fp.route_slot = rp.route_slot;
   fp.inter = reinterpret_cast<uint16_t*>(ws + fg.off_inter);
-  fp.acc = rp.acc;
-  fp.ybuf = reinterpret_cast<float*>(ws + fg.off_ybuf);
-  fp.fc2_arrivals = reinterpret_cast<int32_t*>(ws + fg.off_arrivals);
+  fp.x16 = rp.x16;
+  fp.xexp = rp.xexp;
+  fp.y = reinterpret_cast<float*>(ws + fg.off_y);
   fp.cap_blocks = pg.cap_blocks;
 
   if (events) (void)hipEventRecord(events[0], stream);

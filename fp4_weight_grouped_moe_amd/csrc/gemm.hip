@@ -2,21 +2,24 @@
 //
 // FlashInfer PR 4255, Description: cooperative persistent launches for the fused FC1/FC2
 // kernel with occupancy-aware tiles; Performance: at m = 2048 the old kernel stalled on
-// grid-wide barriers because it was not launched cooperatively. Here FC1 -> FC2 -> cast
-// are ordered by stream order between persistent launches, so no workgroup ever waits
-// for another one that might not be resident.
+// grid-wide barriers because it was not launched cooperatively. Here FC1 -> FC2 -> combine
+// are ordered by stream order between persistent launches, so no workgroup ever waits for
+// another one that might not be resident.
 //
-// M tiles are up to 8 route blocks (128 rows) of one expert; N tiles are 16 row groups
-// (256 weight rows). Each of the 4 waves owns 4 row groups: it streams their E2M1
-// fragments with 128-bit loads one K block ahead, dequantises them in registers into
-// MFMA A operands, and reads the activation rows (B operand) from a double-buffered LDS
-// tile that the whole workgroup stages. Route blocks past the tile's live rows issue no
-// MFMA.
-//  * FC1 epilogue: expert FC1 global scale, SiLU-SwiGLU (gate and up fragments sit in
-//    the same lanes) or relu2, times router weight and the expert's FC2 global scale,
-//    bf16 store into the intermediate workspace row of the route.
-//  * FC2 epilogue: the top-k sum -- fp32 atomic adds of the weighted rows into the
-//    token's accumulator row; a last pass casts the accumulator to bf16.
+// Items are (M tile, N tile) pairs: an M tile is up to 8 route blocks (128 rows) of one
+// expert, an N tile 16 row groups (256 weight rows). One 8-wave workgroup per CU, two waves
+// per SIMD: a wave's dequantisation (VALU) overlaps the other wave's MFMAs -- one wave alone
+// cannot overlap its own. The tile's activation K blocks stream through a ring of LDS stages
+// filled by buffer loads that write LDS directly; each wave streams its own two row groups'
+// E2M1 fragments and scales into a register ring of the same depth, dequantises them in
+// registers into MFMA A operands and reads activation fragments (B operands) from the stage.
+//  * FC1 epilogue: expert FC1 global scale, SiLU-SwiGLU (gate and up fragments sit in the
+//    same lanes) or relu2, times router weight and the expert's FC2 global scale, bf16 store
+//    into the intermediate row of the route's slot.
+//  * FC2 epilogue: the weighted row of each route in fp32; the combine pass sums each
+//    token's top-k rows in a fixed order (deterministic, no atomics) and casts to bf16.
+// NVFP4 FC1 runs on f16 operands: activations pre-scaled per token by a power of two, E2M1 x
+// E4M3 products exact in f16 (half the dequantisation work of the bf16 route).
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -27,19 +30,26 @@ namespace moe {
 
 namespace {
 
-constexpr int kGemmThreads = 256;
+constexpr int kGemmThreads = 512;                       // 8 waves, two per SIMD
+constexpr int kGemmWaves = kGemmThreads / 64;
 constexpr uint32_t kOutOfRange = 0x80000000u;           // set in a buffer offset: past every num_records, loads 0
 constexpr int kRowBytes = kKBlock * 2;                  // one activation row of a K block: 256 B
-constexpr int kWaveW = 4 * kFragBytes;                  // one wave's four fragment blocks of a K block
-constexpr int kLdsBytes = 147456;                       // the pipeline ring (144 KiB of the 160 KiB LDS)
+constexpr int kBlockBytes = kBlockM * kRowBytes;        // one route block of a K block: 4 KiB
+constexpr int kLdsBytes = 131072;                       // the activation stage ring
 
-// Ring of K-block stages in LDS, filled by buffer loads that write LDS directly (no register
-// staging): an activation tile of 16 NB rows x 256 B, then each wave's 4 fragment blocks.
+// Wave layout and pipeline depth for tiles of NB route blocks: the 8 waves split the N tile,
+// 2 row groups x NB blocks each, so every fragment is loaded and dequantised by exactly one
+// wave, straight into its registers. The activation K block of the tile goes through a ring
+// of LDS stages (layout at the activation loads below).
 template <int NB>
-struct Ring {
-  static constexpr int kStage = NB * kBlockM * kRowBytes + 4 * kWaveW;
-  static constexpr int kDepth = kLdsBytes / kStage;                  // 3 (NB 8) .. 7 (NB 1)
-  static constexpr int kLoads = NB + 4 + 4;                          // vector loads a wave issues per stage
+struct Plan {
+  static constexpr int FR = 2;                                      // row groups per wave
+  static constexpr int BW = NB;                                     // route blocks per wave
+  static constexpr int XD = NB >= 2 ? NB / 2 : 1;                   // activation loads per wave (NB 1: waves 4-7 repeat 0-3)
+  static constexpr int kStage = NB * kBlockBytes;
+  static constexpr int kDepth = kLdsBytes / kStage < 6 ? kLdsBytes / kStage : 6;   // 4 (NB 8), else 6
+  static constexpr int kLoads = XD + 2 * FR;                        // vector loads a wave issues per stage
+  static_assert(kDepth >= 3 && (kDepth - 2) * kLoads < 64, "ring too shallow or vmcnt out of range");
 };
 
 // s_waitcnt with only the vector-memory counter bounded (gfx9 encoding: vmcnt in bits 3:0
@@ -69,6 +79,7 @@ __device__ __forceinline__ void* uniform_ptr(const void* p) {
   return reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
 }
 
+// 16 bytes per lane from a buffer into LDS at lds_dst + 16 * lane.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const uint8_t* lds_dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, int(voff), 0, 0, 0);
 }
@@ -79,16 +90,50 @@ struct GemmCtx {
   int64_t sc_per_group;
   const uint8_t* nib;
   const uint8_t* scb;
-  __amdgpu_buffer_rsrc_t act;        // x (FC1) or the intermediate rows (FC2), bounds-checked
+  __amdgpu_buffer_rsrc_t act;        // activations (x, its f16 copy, or the intermediate rows), bounds-checked
   int act_row_bytes, k_bytes;        // row pitch of that buffer and its K extent, in bytes
 };
 
-// One item: NB route blocks (16 NB rows) of one expert x 256 weight rows (16 row groups,
-// 4 per wave), full K.
+// Dequantisation of one wave's fragment dword for MFMA step s, for the three routes:
+// NVFP4 to f16 (pow2 by the scaled convert, mantissa by one packed f16 multiply), NVFP4 to
+// bf16 through f32, MXFP4 to bf16 (the scaled convert alone).
+// Each keeps the raw scale dword and decodes the scale of step s on use (fewer live
+// registers than four decoded scales).
+template <int FMT, bool F16>
+struct Deq {
+  typedef bf16x8 T;
+  uint32_t w;
+  __device__ __forceinline__ void set(uint32_t v) { w = v; }
+  __device__ __forceinline__ T operator()(uint32_t q, int s) const {
+    if (FMT == FMT_NVFP4) {
+      const f32x2 pr = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s >= 2 ? w >> 16 : w, 1.0f, false);
+      return dq8<FMT>(q, pr[s & 1]);
+    }
+    return dq8<FMT>(q, __uint_as_float(((w >> (8 * s)) & 0xFFu) << 23));
+  }
+};
+template <>
+struct Deq<FMT_NVFP4, true> {
+  typedef f16x8 T;
+  uint32_t w;
+  __device__ __forceinline__ void set(uint32_t v) { w = v; }
+  __device__ __forceinline__ T operator()(uint32_t q, int s) const {
+    const f32x2 pr = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s >= 2 ? w >> 16 : w, 1.0f, false);
+    return dq8_nv_f16(q, split_nv_scale(pr[s & 1]));
+  }
+};
+
+__device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, const f32x4& c) { return mfma16(a, b, c); }
+__device__ __forceinline__ f32x4 mma(const f16x8& a, const f16x8& b, const f32x4& c) { return mfma16h(a, b, c); }
+
+// One item: NB route blocks (16 NB rows) of one expert x 256 weight rows, full K.
 template <int FMT, int PHASE, int NB>
 __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c, uint8_t* lds, int mt, int nt) {
-  using R = Ring<NB>;
-  constexpr int D = R::kDepth;
+  using P = Plan<NB>;
+  constexpr int D = P::kDepth, FR = P::FR, BW = P::BW, XD = P::XD;
+  constexpr bool F16 = FMT == FMT_NVFP4 && PHASE == 1;
+  using Dq = Deq<FMT, F16>;
+  using T = typename Dq::T;
   const PreparedGeom& g = p.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int2 tile = p.tiles[mt];
@@ -97,126 +142,118 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
   const int e = __builtin_amdgcn_readfirstlane(tile.y >> 8);
   const int kbs = c.kbs;
 
-  // Activation rows. Load j of wave w fills tile rows 4q .. 4q+3 (q = w NB + j), lane l the
-  // 16-byte chunk position l % 16 of row 4q + l / 16 with the row's chunk (l % 16) ^ (row % 16):
-  // the XOR swizzle lets the 16 lanes that read one chunk column of 16 rows hit 16 distinct
-  // bank groups. Padding slots and blocks past the tile read 0 through the bounds check.
-  uint32_t src[NB], chunk[NB];
+  // Activation loads. A route block's K block (16 rows x 256 B) sits in LDS as 32 half-row
+  // slots of 128 B: row r = 8 r3 + r7, half h goes to slot 4 r7 + 2 h + r3, and its 16-byte
+  // chunk c to position c ^ r7 inside the slot. Load q (1 KiB) of a stage fills slots
+  // 8 (q % 4) .. +7 of block q / 4 -- four whole rows, so every load reads eight full 128-byte
+  // lines -- and the 16 lanes that later read one chunk column of 16 rows hit 16 distinct
+  // bank groups. Padding slots and blocks past the tile read 0 through the bounds check, so no
+  // load is predicated.
+  uint32_t rowoff[XD], gofs[XD];
+  int qdst[XD];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int row = 4 * (wave * NB + j) + (lane >> 4);
+  for (int j = 0; j < XD; ++j) {
+    const int q = NB >= 2 ? wave * XD + j : (wave & 3);
+    const int hslot = 8 * (q & 3) + (lane >> 3);            // half-row slot of this lane
+    const int r7 = hslot >> 2, h = (hslot >> 1) & 1, r3 = hslot & 1;
+    const int row = (q >> 2) * kBlockM + 8 * r3 + r7;
     const int64_t slot = fb * kBlockM + row;
     const int t = row < nb * kBlockM ? p.slot_info[slot].x : -1;
     const int64_t src_row = PHASE == 1 ? int64_t(t) : slot;   // x row of the token, or the slot's own row
-    chunk[j] = uint32_t((lane & 15) ^ (row & 15)) << 4;
-    src[j] = t >= 0 ? uint32_t(src_row * c.act_row_bytes) + chunk[j] : kOutOfRange;
+    qdst[j] = q * 1024;
+    gofs[j] = uint32_t(8 * h + ((lane & 7) ^ r7)) << 4;
+    rowoff[j] = t >= 0 ? uint32_t(src_row * c.act_row_bytes) : kOutOfRange;
   }
-  // This wave's four row groups are contiguous in the prepared buffer; groups past the end
-  // (last N tile only) fall outside the resource and read 0.
-  const int rg_base = nt * 16 + wave * 4;
-  const int live_groups = max(0, min(4, c.groups - rg_base));
+  // This wave's row groups 2w, 2w+1 of the N tile: fragment blocks and scale rows through
+  // buffer resources over the tile's groups, so groups past the end (last N tile only) read
+  // 0 and are never stored.
+  const int tile_groups = min(16, c.groups - nt * 16);
+  const int64_t g0 = int64_t(e) * c.groups + nt * 16;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      uniform_ptr(c.nib + (int64_t(e) * c.groups + min(rg_base, c.groups - 1)) * kbs * kFragBytes), 0,
-      __builtin_amdgcn_readfirstlane(live_groups * kbs * kFragBytes), 0x00020000);
-  const uint8_t* sgp[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int rg = min(rg_base + f, c.groups - 1);
-    sgp[f] = c.scb + (int64_t(e) * c.groups + rg) * c.sc_per_group;
-  }
+      uniform_ptr(c.nib + g0 * kbs * kFragBytes), 0,
+      __builtin_amdgcn_readfirstlane(tile_groups * kbs * kFragBytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(c.scb + g0 * c.sc_per_group), 0,
+      __builtin_amdgcn_readfirstlane(int(tile_groups * c.sc_per_group)), 0x00020000);
+  const int rg_base = nt * 16 + wave * FR;
   const int sc_lane = FMT == FMT_NVFP4 ? ((lane >> 5) * 16 + (lane & 15)) * 16 : (lane & 15) * 16;
 
-  // One stage: the activation K block and this wave's weight K block into LDS slot `slot`, its
+  // One stage: the activation K block into LDS slot `slot`, this wave's fragment dwords and
   // scale dwords into registers. Blocks past K are clamped (weights) or read 0 (activations):
-  // every stage issues the same R::kLoads loads, so the vmcnt arithmetic below is exact.
-  uint32_t sc[D][4];
-  auto issue = [&](int kb, int slot, uint32_t* scd) {
-    uint8_t* st = lds + slot * R::kStage;
+  // every stage issues the same P::kLoads loads per wave, so the vmcnt arithmetic below is
+  // exact.
+  u32x4 wr[D][FR];
+  uint32_t sc[D][FR];
+  auto issue = [&](int kb, int slot, u32x4* wd, uint32_t* scd) {
+    uint8_t* st = lds + slot * P::kStage;
     const uint32_t k = uint32_t(kb) * kRowBytes;
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      dma16(c.act, st + (wave * NB + j) * 1024, (src[j] + k) | (k + chunk[j] < uint32_t(c.k_bytes) ? 0u : kOutOfRange));
+    for (int j = 0; j < XD; ++j)
+      dma16(c.act, st + qdst[j], (rowoff[j] + k + gofs[j]) | (k + gofs[j] < uint32_t(c.k_bytes) ? 0u : kOutOfRange));
     const int kc = min(kb, kbs - 1);
-    uint8_t* wst = st + NB * kBlockM * kRowBytes + wave * kWaveW;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) dma16(wres, wst + f * kFragBytes, uint32_t((f * kbs + kc) * kFragBytes + lane * 16));
+    for (int f = 0; f < FR; ++f)
+      wd[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          wres, ((wave * FR + f) * kbs + kc) * kFragBytes + lane * 16, 0, 0));
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-      scd[f] = *reinterpret_cast<const uint32_t*>(sgp[f] + int64_t(kc >> 2) * g.sc_chunk_bytes + sc_lane + (kc & 3) * 4);
+    for (int f = 0; f < FR; ++f)
+      scd[f] = __builtin_amdgcn_raw_buffer_load_b32(
+          sres, int((wave * FR + f) * c.sc_per_group + (kc >> 2) * g.sc_chunk_bytes) + sc_lane + (kc & 3) * 4, 0, 0);
   };
 
-  f32x4 acc[4][NB];
+  f32x4 acc[FR][BW];
 #pragma unroll
-  for (int f = 0; f < 4; ++f)
+  for (int f = 0; f < FR; ++f)
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < BW; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // One K block: four MFMA K-steps. The activation reads and dequantisation of step s+1 are
-  // issued ahead of the MFMAs of step s, and the scheduler is asked to interleave them one
-  // MFMA at a time so the matrix pipe stays busy while LDS and the VALU work.
-  constexpr int kDqValu = FMT == FMT_NVFP4 ? 16 : 4;           // VALU ops of one dq8
-  constexpr int kValuPerMfma = (4 * kDqValu + 4 * NB - 1) / (4 * NB);
-  auto compute = [&](int slot, const uint32_t* scd) {
-    const uint8_t* st = lds + slot * R::kStage;
-    const uint8_t* xrow = st + (lane & 15) * kRowBytes;
-    const int sw = lane & 15;
-    u32x4 wq[4];
+  // One K block: four MFMA K-steps.
+  auto compute = [&](int slot, const u32x4* wq, const uint32_t* scd) {
+    const uint8_t* st = lds + slot * P::kStage;
+    Dq dq[FR];
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
-      wq[f] = *reinterpret_cast<const u32x4*>(st + NB * kBlockM * kRowBytes + wave * kWaveW + f * kFragBytes + lane * 16);
-    float scl[4][4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) decode_scales<FMT>(scd[f], scl[f]);
+    for (int f = 0; f < FR; ++f) dq[f].set(scd[f]);
+    // Lane l reads chunk 4 s + l / 16 of row l % 16: slot 4 r7 + 2 (s / 2) + r3, position
+    // (4 (s % 2) + l / 16) ^ r7 -- two lane bases (even and odd s) plus immediates.
+    const int r7 = lane & 7, r3 = (lane >> 3) & 1, q4 = lane >> 4;
+    const uint8_t* xb_even = st + r7 * 512 + r3 * 128 + ((q4 ^ r7) << 4);
+    const uint8_t* xb_odd = st + r7 * 512 + r3 * 128 + (((4 + q4) ^ r7) << 4);
     auto xread = [&](int b, int s) {
-      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-          xrow + b * kBlockM * kRowBytes + (((4 * s + (lane >> 4)) ^ sw) << 4)));
+      return __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>((s & 1 ? xb_odd : xb_even) + b * kBlockBytes +
+                                                                   (s >> 1) * 256));
     };
-    bf16x8 xb[2][NB], a[2][4];
-#pragma unroll
-    for (int b = 0; b < NB; ++b) xb[0][b] = xread(b, 0);
-#pragma unroll
-    for (int f = 0; f < 4; ++f) a[0][f] = dq8<FMT>(wq[f][0], scl[f][0]);
+    // Two waves share each SIMD, so LDS latency is hidden by the other wave: the activation
+    // fragments of a K-step are read just before its MFMAs (no double buffer, no spills).
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int cur = s & 1, nxt = cur ^ 1;
-      if (s < 3) {
+      T xb[BW], a[FR];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) xb[nxt][b] = xread(b, s + 1);
+      for (int b = 0; b < BW; ++b) xb[b] = xread(b, s);
 #pragma unroll
-        for (int f = 0; f < 4; ++f) a[nxt][f] = dq8<FMT>(wq[f][s + 1], scl[f][s + 1]);
-      }
+      for (int f = 0; f < FR; ++f) a[f] = dq[f](wq[f][s], s);
 #pragma unroll
-      for (int b = 0; b < NB; ++b)
+      for (int b = 0; b < BW; ++b)
 #pragma unroll
-        for (int f = 0; f < 4; ++f) acc[f][b] = mfma16(a[cur][f], xb[cur][b], acc[f][b]);
-      if (s < 3) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // one LDS read
-#pragma unroll
-          for (int f = 0; f < 4; ++f) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);    // dequant VALU
-          }
-        }
-      }
+        for (int f = 0; f < FR; ++f) acc[f][b] = mma(a[f], xb[b], acc[f][b]);
+      // Keep the scheduler from hoisting the next K-steps' reads (register pressure).
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // Pipeline: stages 0 .. D-2 in flight before the loop; step kb waits until its own stage has
   // landed (at most D-2 later stages still outstanding), meets the other waves at a barrier
   // (their loads have landed too, and all are done with slot (kb-1) % D), refills that slot
-  // with stage kb+D-1 and computes stage kb. Barriers order LDS only.
+  // with stage kb+D-1 and computes stage kb.
   auto step = [&](int kb, int j) {
-    wait_vmcnt<(D - 2) * R::kLoads>();
+    wait_vmcnt<(D - 2) * P::kLoads>();
     stage_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(kb + D - 1, (j + D - 1) % D, sc[(j + D - 1) % D]);
+    issue(kb + D - 1, (j + D - 1) % D, wr[(j + D - 1) % D], sc[(j + D - 1) % D]);
     __builtin_amdgcn_sched_barrier(0);
-    compute(j, sc[j]);
+    compute(j, wr[j], sc[j]);
   };
 #pragma unroll
-  for (int j = 0; j < D - 1; ++j) issue(j, j, sc[j]);
+  for (int j = 0; j < D - 1; ++j) issue(j, j, wr[j], sc[j]);
   __builtin_amdgcn_sched_barrier(0);
   int kb = 0;
   for (; kb + D <= kbs; kb += D) {
@@ -235,36 +272,39 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
   if (PHASE == 1) {
     const float g13 = p.g13[e], g2 = p.g2[e];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    for (int bb = 0; bb < BW; ++bb) {
+      const int b = bb;
       if (b < nb) {
         const int64_t slot = (fb + b) * kBlockM + col;
         const int2 info = p.slot_info[slot];
-        const float rw = info.x >= 0 ? __int_as_float(info.y) * g2 : 0.f;
+        const bool valid = info.x >= 0;
+        const float rw = valid ? __int_as_float(info.y) * g2 : 0.f;
+        const float s13 = F16 && valid ? ldexpf(g13, p.xexp[info.x]) : g13;
         uint16_t* dst = p.inter + slot * g.ip;
         if (g.act == ACT_SWIGLU) {
 #pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
+          for (int pr = 0; pr < FR / 2; ++pr) {
             if (rg_base + 2 * pr < c.groups) {
-              float a[4];
+              float v[4];
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                a[i] = silu_f32(acc[2 * pr][b][i] * g13) * (acc[2 * pr + 1][b][i] * g13) * rw;
+                v[i] = silu_f32(acc[2 * pr][bb][i] * s13) * (acc[2 * pr + 1][bb][i] * s13) * rw;
               const int64_t icol = int64_t((rg_base + 2 * pr) >> 1) * 16 + r0;
-              *reinterpret_cast<uint2*>(dst + icol) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+              *reinterpret_cast<uint2*>(dst + icol) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }
           }
         } else {
 #pragma unroll
-          for (int f = 0; f < 4; ++f) {
+          for (int f = 0; f < FR; ++f) {
             if (rg_base + f < c.groups) {
-              float a[4];
+              float v[4];
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const float u = fmaxf(acc[f][b][i] * g13, 0.f);
-                a[i] = u * u * rw;
+                const float u = fmaxf(acc[f][bb][i] * s13, 0.f);
+                v[i] = u * u * rw;
               }
               const int64_t icol = int64_t(rg_base + f) * 16 + r0;
-              *reinterpret_cast<uint2*>(dst + icol) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+              *reinterpret_cast<uint2*>(dst + icol) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
             }
           }
         }
@@ -272,20 +312,15 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
     }
   } else {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
+    for (int bb = 0; bb < BW; ++bb) {
+      const int b = bb;
       if (b < nb) {
-        const int64_t slot = (fb + b) * kBlockM + col;
-        const int t = p.slot_info[slot].x;
-        if (t >= 0) {
+        const int r = p.sorted_route_ids[(fb + b) * kBlockM + col];
+        if (r >= 0) {
 #pragma unroll
-          for (int f = 0; f < 4; ++f) {
-            if (rg_base + f < c.groups) {
-              const int64_t h = int64_t(rg_base + f) * 16 + r0;
-              float* dst = p.acc + int64_t(t) * g.H + h;
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (h + i < g.H) atomicAdd(dst + i, acc[f][b][i]);
-            }
+          for (int f = 0; f < FR; ++f) {
+            const int64_t h = int64_t(rg_base + f) * 16 + r0;
+            if (h < g.H) *reinterpret_cast<f32x4*>(p.y + int64_t(r) * g.H + h) = acc[f][bb];
           }
         }
       }
@@ -304,9 +339,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
   c.scb = PHASE == 1 ? p.sc1 : p.sc2;
   c.sc_per_group = PHASE == 1 ? g.sc1_per_group : g.sc2_per_group;
   if (PHASE == 1) {
+    const uint16_t* src = FMT == FMT_NVFP4 ? p.x16 : p.x;
     c.act_row_bytes = g.H * 2;
     c.k_bytes = g.H * 2;
-    c.act = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x), 0, int(int64_t(p.m) * g.H * 2), 0x00020000);
+    c.act = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src), 0, int(p.m * g.H * 2), 0x00020000);
   } else {
     c.act_row_bytes = int(g.ip * 2);
     c.k_bytes = int(g.ip * 2);
@@ -314,18 +350,34 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
   }
   const int n_mt = p.live[4];
   const int n_nt = (c.groups + 15) / 16;
-  const int n_items = n_mt * n_nt;
-  // Persistent workgroups take items from a queue (reset by the route packer) in M-tile
-  // order, N fastest: the workgroups that share an activation tile, and the consecutive M
-  // tiles of one expert that share its weight tiles, run at the same time, so the re-reads
-  // hit the caches; full tiles are queued first, so the load stays balanced to the end.
+  // Persistent workgroups take items from per-XCD queues (reset by the route packer). Queue x
+  // holds the M tiles mt = x mod 8 (full tiles come first in the tile table), each as its
+  // N tiles in a row; workgroups are dealt to the XCDs round robin, so the ~32 workgroups of
+  // an XCD run two M tiles at a time and fetch each activation K block into their shared L2
+  // once. The same expert's M tiles on the other XCDs read its weight tiles at the same
+  // time, which the Infinity Cache serves. An exhausted queue sends a workgroup on to the
+  // next one, so the load stays balanced to the end.
   __shared__ int s_item;
-  int* queue = p.live + (PHASE == 1 ? 5 : 6);
+  int* queues = p.live + (PHASE == 1 ? 8 : 16);
+  int q = blockIdx.x & 7, tried = 0;                 // thread 0's queue cursor
   for (;;) {
-    if (threadIdx.x == 0) s_item = atomicAdd(queue, 1);
+    if (threadIdx.x == 0) {
+      int found = -1;
+      while (tried < 8) {
+        const int len = n_mt > q ? ((n_mt - 1 - q) / 8 + 1) * n_nt : 0;
+        const int i = atomicAdd(&queues[q], 1);
+        if (i < len) {
+          found = (q + 8 * (i / n_nt)) * n_nt + i % n_nt;
+          break;
+        }
+        q = (q + 1) & 7;
+        ++tried;
+      }
+      s_item = found;
+    }
     lds_barrier();
     const int item = __builtin_amdgcn_readfirstlane(s_item);
-    if (item >= n_items) break;
+    if (item < 0) break;
     // Every item starts with a barrier after this read, so thread 0 cannot overwrite
     // s_item before all threads have taken it.
     const int mt = item / n_nt, nt = item % n_nt;
@@ -338,17 +390,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
   }
 }
 
-// out[i] = bf16(acc[i]) for the m x H accumulator.
-__global__ void finalize_kernel(const float* __restrict__ acc, uint16_t* __restrict__ out, int64_t n) {
-  const int64_t n2 = n / 2;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n2; i += int64_t(gridDim.x) * blockDim.x) {
-    const float2 v = reinterpret_cast<const float2*>(acc)[i];
-    reinterpret_cast<uint32_t*>(out)[i] = pack_bf16x2(v.x, v.y);
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0 && (n & 1)) {
-    bf16x2 v;
-    v[0] = (__bf16)acc[n - 1];
-    out[n - 1] = __builtin_bit_cast(uint16_t, v[0]);
+// out[t] = bf16(sum over the token's valid routes of y[route]) in route order j = 0..k-1.
+__global__ void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ route_slot,
+                               uint16_t* __restrict__ out, int64_t m, int topk, int64_t H) {
+  const int64_t q = H / 4;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < m * q; i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t t = i / q, c4 = (i % q) * 4;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < topk; ++j) {
+      const int64_t r = t * topk + j;
+      if (route_slot[r] >= 0) s += *reinterpret_cast<const f32x4*>(y + r * H + c4);
+    }
+    *reinterpret_cast<uint2*>(out + t * H + c4) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
   }
 }
 
@@ -363,7 +416,7 @@ hipError_t allow_large_lds(size_t lds) {
 }
 
 hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks) {
-  // One 4-wave workgroup per CU: 128 accumulator AGPRs + ~230 VGPRs per wave leave room for one.
+  // One 8-wave workgroup per CU (two waves per SIMD, up to 256 registers each).
   const int grid = num_cus;
   const size_t lds = kLdsBytes;
   hipError_t e = p.g.fmt == FMT_NVFP4 ? allow_large_lds<FMT_NVFP4, 1>(lds) : allow_large_lds<FMT_MXFP4, 1>(lds);
@@ -376,11 +429,11 @@ hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hi
   if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   if (marks) (void)hipEventRecord(marks[1], stream);
-  const int64_t n = p.m * p.g.H;
-  int64_t fb = (n / 2 + 255) / 256;
-  if (fb < 1) fb = 1;
-  if (fb > 4096) fb = 4096;
-  hipLaunchKernelGGL(finalize_kernel, dim3(fb), dim3(256), 0, stream, p.acc, p.out, n);
+  const int64_t n = p.m * p.g.H / 4;
+  int64_t cb = (n + 255) / 256;
+  if (cb < 1) cb = 1;
+  if (cb > 8192) cb = 8192;
+  hipLaunchKernelGGL(combine_kernel, dim3(cb), dim3(256), 0, stream, p.y, p.route_slot, p.out, p.m, p.topk, int64_t(p.g.H));
   if (marks) (void)hipEventRecord(marks[2], stream);
   return hipGetLastError();
 }

@@ -18,14 +18,16 @@ struct RoutePackParams {
   int32_t* expert_offsets;
   int32_t* sorted_route_ids;
   int32_t* block_expert;
-  int32_t* live;                 // [8]: valid, padded, live blocks, m, M tiles, two queue counters
+  int32_t* live;                 // [64]: valid, padded, live blocks, m, M tiles; [8..23] GEMM queues
   int32_t* route_slot;
   int2* tiles;                   // [cap_blocks] (first block, blocks | expert << 8) or null
   int2* slot_info;               // [cap_routes] (token, router weight bits) or null
-  float* acc;                    // fp32 accumulator cleared by the extra workgroups, or null
-  int64_t acc_elems;
-  int32_t* zero_ints;            // counters cleared by the packing workgroup, or null
-  int64_t n_zero_ints;
+  // Side work of the extra workgroups (grouped-GEMM path with NVFP4 weights): activation
+  // rows to f16 times a per-token power of two, or null.
+  const uint16_t* x;             // bf16 [m, hidden]
+  uint16_t* x16;                 // f16 [m, hidden]
+  int32_t* xexp;                 // [m] exponent p: x = x16 * 2^p
+  int64_t hidden;
 };
 
 struct PrepareParams {
@@ -54,23 +56,24 @@ struct FusedParams {
   int32_t topk;
   const int32_t* sorted_route_ids;
   const int32_t* block_expert;
-  int32_t* live;                 // route-pack counts; [5], [6] = grouped-GEMM work queues
+  int32_t* live;                 // route-pack counts; [8..15] FC1, [16..23] FC2 work queues
   const int2* tiles;
   const int2* slot_info;
   const int32_t* route_slot;      // [m * topk] packed slot of each route or -1
   uint16_t* inter;               // bf16 [cap_routes, ip]
-  float* acc;                    // fp32 [m, H] (grouped GEMM)
-  float* ybuf;                   // fp32 [cap_routes, hp] route partials (decode)
-  int32_t* fc2_arrivals;         // [hp / 64] decode FC2 arrival counters, zero on entry
+  const uint16_t* x16;           // f16 [m, H] scaled activations (grouped GEMM, NVFP4)
+  const int32_t* xexp;           // [m] their per-token exponents
+  float* y;                      // fp32 [m * topk, H] weighted FC2 rows per route (grouped GEMM)
   int64_t cap_blocks;
   int64_t lds_block_table;       // decode FC1: bytes of LDS before the staged activations
 };
 
 size_t route_pack_lds_bytes(int num_experts);
-hipError_t launch_route_pack(const RoutePackParams& p, int zero_blocks, hipStream_t stream);
+// `side_blocks` extra workgroups do the activation conversion when p.x16 is set.
+hipError_t launch_route_pack(const RoutePackParams& p, int side_blocks, hipStream_t stream);
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
-// `marks` (nullable) receives an event record after each kernel: FC1, FC2, final cast
-// (the decode path records its last mark right after FC2).
+// `marks` (nullable) receives an event record after each kernel: FC1, FC2, then the top-k
+// combine (the decode path records its last mark right after FC2).
 hipError_t launch_decode(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks);
 hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks);
 

@@ -87,7 +87,7 @@ __host__ __device__ inline PackGeom make_pack_geom(int64_t cap, int64_t k, int64
   p.off_offsets = o;      o = align256(o + size_t(E + 1) * 4);
   p.off_sorted = o;       o = align256(o + size_t(p.cap_routes) * 4);
   p.off_block_expert = o; o = align256(o + size_t(p.cap_blocks) * 4);
-  p.off_live = o;         o = align256(o + 8 * 4);   // live[0..3] public, [4] = M tiles
+  p.off_live = o;         o = align256(o + 64 * 4);  // [0..3] public, [4] M tiles, [8..23] GEMM queues
   p.off_route_slot = o;   o = align256(o + size_t(routes) * 4);
   // fused-layer extras: M-tile table (first block, block count) and token + weight per slot
   p.off_tiles = o;        o = align256(o + size_t(p.cap_blocks) * 8);
@@ -98,28 +98,24 @@ __host__ __device__ inline PackGeom make_pack_geom(int64_t cap, int64_t k, int64
 
 constexpr int kDecodeMaxM = 16;          // token columns of the decode path
 constexpr int kDecodeStageBytes = 65536; // LDS for the decode kernels' staged activation rows
-constexpr int kFc2RangeRows = 64;        // hidden rows per decode FC2 arrival counter
 
-// Fused-layer workspace: route pack (block 16) + bf16 intermediate + fp32 output
-// accumulator (grouped GEMM) + fp32 route partials and arrival counters (decode, only when
-// the capacity admits the decode path).
+// Fused-layer workspace: route pack (block 16), bf16 intermediate rows per packed slot,
+// and for the grouped-GEMM path the f16 copy of the activations with per-token exponents
+// (NVFP4) and the fp32 FC2 row of every route, summed over top-k by the combine pass.
 struct FusedGeom {
   PackGeom pack;
-  size_t off_pack, off_inter, off_acc, off_ybuf, off_arrivals, total;
-  int64_t n_arrivals;
+  size_t off_pack, off_inter, off_x16, off_xexp, off_y, total;
 };
 
 __host__ __device__ inline FusedGeom make_fused_geom(const PreparedGeom& w, int64_t cap, int64_t k) {
   FusedGeom f{};
   f.pack = make_pack_geom(cap, k, w.E, kBlockM);
-  const bool decode = cap <= kDecodeMaxM;
-  f.n_arrivals = decode ? ceil_div(w.hp, kFc2RangeRows) : 0;
   size_t o = 0;
-  f.off_pack = o;     o = align256(o + f.pack.total);
-  f.off_inter = o;    o = align256(o + size_t(f.pack.cap_routes) * w.ip * 2);
-  f.off_acc = o;      o = align256(o + size_t(cap) * w.H * 4);
-  f.off_ybuf = o;     o = align256(o + (decode ? size_t(f.pack.cap_routes) * w.hp * 4 : 0));
-  f.off_arrivals = o; o = align256(o + size_t(f.n_arrivals) * 4);
+  f.off_pack = o;  o = align256(o + f.pack.total);
+  f.off_inter = o; o = align256(o + size_t(f.pack.cap_routes) * w.ip * 2);
+  f.off_x16 = o;   o = align256(o + size_t(cap) * w.H * 2);
+  f.off_xexp = o;  o = align256(o + size_t(cap) * 4);
+  f.off_y = o;     o = align256(o + size_t(cap) * k * w.H * 4);
   f.total = o;
   return f;
 }

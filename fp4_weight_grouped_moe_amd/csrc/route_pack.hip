@@ -1,8 +1,10 @@
 // Route packing on gfx950: group token x expert routes by local expert into a padded,
 // power-of-two-capacity workspace (FlashInfer PR 4255, Description: shape-stable route
 // packing; Tests: expert_map and invalid expert ids). One 1024-thread workgroup does the
-// whole pack; every other workgroup of the same launch clears the fp32 output
-// accumulator of the grouped-GEMM path so that no separate launch is needed.
+// whole pack; for the grouped-GEMM path with NVFP4 weights every other workgroup of the
+// same launch converts the activation rows to f16 (exact up to f16 subnormals, below
+// 2^-38 of the row maximum) times a per-token power of two, so that no separate launch is
+// needed.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -66,7 +68,6 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   for (int e = tid; e < E; e += kPackThreads) cnt[e] = 0;
   if (tid == 0) wave_tot[kPackWaves + 4] = 0;
   for (int i = tid; i < kPackWaves * E; i += kPackThreads) wcnt[i] = 0;
-  for (int64_t i = tid; i < p.n_zero_ints; i += kPackThreads) p.zero_ints[i] = 0;
   __syncthreads();
   if (l_first >= 0) atomicAdd(&cnt[l_first], 1);
   for (int64_t r = kPackThreads + tid; r < p.num_routes; r += kPackThreads) {
@@ -127,9 +128,8 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
     p.live[2] = total_padded / B;
     p.live[3] = int(p.m);
     p.live[4] = tile_carry;
-    p.live[5] = 0;                                         // grouped-GEMM work queues (FC1, FC2)
-    p.live[6] = 0;
   }
+  if (tid < 16) p.live[8 + tid] = 0;                       // grouped-GEMM work queues: 8 per phase
   for (int64_t s = total_padded + tid; s < p.cap_routes; s += kPackThreads) {
     p.sorted_route_ids[s] = -1;
     if (p.slot_info) p.slot_info[s] = make_int2(-1, 0);
@@ -198,21 +198,51 @@ __global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParam
     pack_routes(p, smem);
     return;
   }
-  // Clear the fp32 accumulator [acc_elems] with 16-byte stores (acc_elems % 4 == 0).
-  float4* acc = reinterpret_cast<float4*>(p.acc);
-  const int64_t n4 = p.acc_elems / 4;
-  const int64_t stride = int64_t(gridDim.x - 1) * blockDim.x;
-  for (int64_t i = int64_t(blockIdx.x - 1) * blockDim.x + threadIdx.x; i < n4; i += stride)
-    acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  // One wave per activation row: row maximum, exponent p with max * 2^-p in [2^14, 2^15),
+  // then the scaled f16 row (hidden % 8 == 0: 16-byte chunks).
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = int64_t(gridDim.x - 1) * (blockDim.x / 64);
+  const int64_t chunks = p.hidden / 8;
+  for (int64_t t = int64_t(blockIdx.x - 1) * (blockDim.x / 64) + (threadIdx.x >> 6); t < p.m; t += waves) {
+    const uint4* row = reinterpret_cast<const uint4*>(p.x + t * p.hidden);
+    float amax = 0.f;
+    for (int64_t c = lane; c < chunks; c += 64) {
+      const uint4 v = row[c];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[i] << 16)), fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
+    int e = 0;
+    if (amax > 0.f && amax <= 3.4e38f) (void)frexpf(amax, &e);   // amax = f * 2^e, f in [0.5, 1)
+    const int pexp = amax > 0.f && amax <= 3.4e38f ? e - 15 : 0;
+    const float inv = ldexpf(1.f, -pexp);
+    uint4* dst = reinterpret_cast<uint4*>(p.x16 + t * p.hidden);
+    for (int64_t c = lane; c < chunks; c += 64) {
+      const uint4 v = row[c];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const _Float16 lo = (_Float16)(__uint_as_float(w[i] << 16) * inv);
+        const _Float16 hi = (_Float16)(__uint_as_float(w[i] & 0xFFFF0000u) * inv);
+        o[i] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+      }
+      dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    if (lane == 0) p.xexp[t] = pexp;
+  }
 }
 
 size_t route_pack_lds_bytes(int num_experts) {
   return size_t(num_experts) * 4 + 32 * 4 + size_t(kPackWaves) * num_experts + 16;
 }
 
-hipError_t launch_route_pack(const RoutePackParams& p, int zero_blocks, hipStream_t stream) {
+hipError_t launch_route_pack(const RoutePackParams& p, int side_blocks, hipStream_t stream) {
   const size_t lds = route_pack_lds_bytes(p.num_experts);
-  hipLaunchKernelGGL(route_pack_kernel, dim3(1 + (p.acc ? zero_blocks : 0)), dim3(kPackThreads), lds, stream, p);
+  hipLaunchKernelGGL(route_pack_kernel, dim3(1 + (p.x16 ? side_blocks : 0)), dim3(kPackThreads), lds, stream, p);
   return hipGetLastError();
 }
 

@@ -142,12 +142,13 @@ int moe_w4a16_prepare(const moe_w4a16_dims* dims, const uint8_t* w13, const uint
  * Reviewer Notes (decode path cap m <= 4 here, m <= 8 upstream).
  *
  * A call whose m is at most the decode threshold and whose token_capacity is at most
- * MOE_DECODE_MAX_M takes the decode path: split-K MFMA kernels, route partials in fp32,
- * and the last FC2 workgroup of each hidden-row range (an atomic arrival count, never a
- * wait) sums every token's routes in a fixed order -- deterministic, no atomics on data.
- * Other calls take the grouped GEMM path: FC1 + activation epilogue, FC2 with fp32
- * atomic adds of the weighted rows, a final bf16 cast. Neither path waits on a
- * workgroup that may not be resident. */
+ * MOE_DECODE_MAX_M takes the decode path: two weight-streaming MFMA kernels; FC2 gives
+ * each workgroup a range of hidden rows for every route and sums each token's routes in
+ * LDS before one bf16 store. Other calls take the grouped-GEMM path: FC1 + activation
+ * epilogue over (route tile, weight tile) items, FC2 writing each route's weighted fp32
+ * row, and a combine pass that sums every token's top-k rows in route order and casts to
+ * bf16 -- deterministic, no atomics on data. Persistent workgroups take items from a
+ * queue; no workgroup waits on another that may not be resident. */
 #define MOE_DECODE_MAX_M 16
 
 /* Workspace bytes for moe_w4a16_fused at a token capacity (route packing included). */
@@ -168,7 +169,7 @@ int moe_w4a16_fused(const moe_w4a16_dims* dims, const void* prepared, size_t pre
 
 /* Measurement twin of moe_w4a16_fused: the same launches on `stream`, with HIP event
  * records between them -- events[0] before route packing, [1] after it, [2] after FC1,
- * [3] after FC2, [4] after the bf16 cast (decode path: [4] right after [3]). The
+ * [3] after FC2, [4] after the top-k combine (decode path: [4] right after [3]). The
  * caller creates the events (num_events >= 5). Not for graph capture. */
 int moe_w4a16_fused_profiled(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes,
                              const uint16_t* x, int64_t m, const int32_t* topk_ids,
