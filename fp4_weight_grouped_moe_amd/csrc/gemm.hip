@@ -49,7 +49,8 @@ struct Plan {
   static constexpr int kStage = NB * kBlockBytes;
   static constexpr int kDepth = kLdsBytes / kStage < 6 ? kLdsBytes / kStage : 6;   // 4 (NB 8), else 6
   static constexpr int kLoads = XD + 2 * FR;                        // vector loads a wave issues per stage
-  static_assert(kDepth >= 3 && (kDepth - 2) * kLoads < 64, "ring too shallow or vmcnt out of range");
+  static_assert(kDepth >= 3 && (kDepth - 1) * kLoads < 64, "ring too shallow or vmcnt out of range");
+  static_assert(XD <= 2 * FR, "the stage wait relies on at least as many register loads as LDS loads");
 };
 
 // s_waitcnt with only the vector-memory counter bounded (gfx9 encoding: vmcnt in bits 3:0
@@ -181,24 +182,36 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
   // One stage: the activation K block into LDS slot `slot`, this wave's fragment dwords and
   // scale dwords into registers. Blocks past K are clamped (weights) or read 0 (activations):
   // every stage issues the same P::kLoads loads per wave, so the vmcnt arithmetic below is
-  // exact.
+  // exact. The loads are issued in four parts, one ahead of each MFMA K-step of the stage
+  // being computed, so that a load queue that is still full stalls a wave between MFMA
+  // groups instead of ahead of all of them.
   u32x4 wr[D][FR];
   uint32_t sc[D][FR];
-  auto issue = [&](int kb, int slot, u32x4* wd, uint32_t* scd) {
+  auto issue_part = [&](int part, int kb, int slot, u32x4* wd, uint32_t* scd) {
     uint8_t* st = lds + slot * P::kStage;
     const uint32_t k = uint32_t(kb) * kRowBytes;
-#pragma unroll
-    for (int j = 0; j < XD; ++j)
-      dma16(c.act, st + qdst[j], (rowoff[j] + k + gofs[j]) | (k + gofs[j] < uint32_t(c.k_bytes) ? 0u : kOutOfRange));
     const int kc = min(kb, kbs - 1);
 #pragma unroll
-    for (int f = 0; f < FR; ++f)
-      wd[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-          wres, ((wave * FR + f) * kbs + kc) * kFragBytes + lane * 16, 0, 0));
+    // Order within a stage: scales, fragments (both needed first), then the activations.
+    for (int l = 0; l < P::kLoads; ++l) {
+      if (l * 4 / P::kLoads != part) continue;
+      if (l < FR) {
+        scd[l] = __builtin_amdgcn_raw_buffer_load_b32(
+            sres, int((wave * FR + l) * c.sc_per_group + (kc >> 2) * g.sc_chunk_bytes) + sc_lane + (kc & 3) * 4, 0, 0);
+      } else if (l < 2 * FR) {
+        const int f = l - FR;
+        wd[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            wres, ((wave * FR + f) * kbs + kc) * kFragBytes + lane * 16, 0, 0));
+      } else {
+        const int j = l - 2 * FR;
+        dma16(c.act, st + qdst[j], (rowoff[j] + k + gofs[j]) | (k + gofs[j] < uint32_t(c.k_bytes) ? 0u : kOutOfRange));
+      }
+    }
+  };
+  auto issue = [&](int kb, int slot, u32x4* wd, uint32_t* scd) {
 #pragma unroll
-    for (int f = 0; f < FR; ++f)
-      scd[f] = __builtin_amdgcn_raw_buffer_load_b32(
-          sres, int((wave * FR + f) * c.sc_per_group + (kc >> 2) * g.sc_chunk_bytes) + sc_lane + (kc & 3) * 4, 0, 0);
+    for (int part = 0; part < 4; ++part) issue_part(part, kb, slot, wd, scd);
+    __builtin_amdgcn_sched_barrier(0);            // stages leave in order
   };
 
   f32x4 acc[FR][BW];
@@ -208,7 +221,8 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
     for (int b = 0; b < BW; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One K block: four MFMA K-steps.
-  auto compute = [&](int slot, const u32x4* wq, const uint32_t* scd) {
+  auto compute = [&](int slot, const u32x4* wq, const uint32_t* scd, int kb_next, int slot_next, u32x4* wd_next,
+                     uint32_t* scd_next) {
     const uint8_t* st = lds + slot * P::kStage;
     Dq dq[FR];
 #pragma unroll
@@ -226,6 +240,7 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
     // fragments of a K-step are read just before its MFMAs (no double buffer, no spills).
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      issue_part(s, kb_next, slot_next, wd_next, scd_next);
       T xb[BW], a[FR];
 #pragma unroll
       for (int b = 0; b < BW; ++b) xb[b] = xread(b, s);
@@ -241,16 +256,19 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
   };
 
   // Pipeline: stages 0 .. D-2 in flight before the loop; step kb waits until its own stage has
-  // landed (at most D-2 later stages still outstanding), meets the other waves at a barrier
-  // (their loads have landed too, and all are done with slot (kb-1) % D), refills that slot
-  // with stage kb+D-1 and computes stage kb.
+  // landed, meets the other waves at a barrier (their loads have landed too, and all are done
+  // with slot (kb-1) % D), then computes stage kb while refilling that slot with stage kb+D-1.
+  // Loads that write LDS and loads that write registers complete in order within each kind
+  // but not with respect to each other (measured on gfx950: counting both kinds let a stage's
+  // activation rows be read before they landed). So the wait leaves at most the later
+  // stages' LDS loads, (D-2) * XD, outstanding: then this stage's LDS loads have landed, and
+  // so have its register loads (at least 4 (D-2) >= (D-2) * XD register loads follow them).
   auto step = [&](int kb, int j) {
-    wait_vmcnt<(D - 2) * P::kLoads>();
+    wait_vmcnt<(D - 2) * XD>();
     stage_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue(kb + D - 1, (j + D - 1) % D, wr[(j + D - 1) % D], sc[(j + D - 1) % D]);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(j, wr[j], sc[j]);
+    const int jn = (j + D - 1) % D;
+    compute(j, wr[j], sc[j], kb + D - 1, jn, wr[jn], sc[jn]);
   };
 #pragma unroll
   for (int j = 0; j < D - 1; ++j) issue(j, j, wr[j], sc[j]);
@@ -350,24 +368,39 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
   }
   const int n_mt = p.live[4];
   const int n_nt = (c.groups + 15) / 16;
-  // Persistent workgroups take items from per-XCD queues (reset by the route packer). Queue x
-  // holds the M tiles mt = x mod 8 (full tiles come first in the tile table), each as its
-  // N tiles in a row; workgroups are dealt to the XCDs round robin, so the ~32 workgroups of
-  // an XCD run two M tiles at a time and fetch each activation K block into their shared L2
-  // once. The same expert's M tiles on the other XCDs read its weight tiles at the same
-  // time, which the Infinity Cache serves. An exhausted queue sends a workgroup on to the
-  // next one, so the load stays balanced to the end.
+  // Persistent workgroups take items from per-XCD queues (reset by the route packer).
+  // Workgroups are dealt to the XCDs round robin; queue x holds the full M tiles and the
+  // partial (tail) M tiles whose table index is x mod 8, alternating one full and one partial
+  // tile, each as its N tiles in a row. So the ~32 workgroups of an XCD run two M tiles at a
+  // time and fetch each activation K block into their shared L2 once, and an MFMA-bound full
+  // tile runs beside a weight-stream-bound partial one, so that HBM and the matrix cores are
+  // busy together. The same expert's M tiles on the other XCDs read its weight tiles at the
+  // same time, which the Infinity Cache serves. An exhausted queue sends a workgroup on to
+  // the next one, so the load stays balanced to the end.
   __shared__ int s_item;
   int* queues = p.live + (PHASE == 1 ? 8 : 16);
+  const int n_full = p.live[5], n_part = n_mt - n_full;
   int q = blockIdx.x & 7, tried = 0;                 // thread 0's queue cursor
   for (;;) {
     if (threadIdx.x == 0) {
       int found = -1;
       while (tried < 8) {
-        const int len = n_mt > q ? ((n_mt - 1 - q) / 8 + 1) * n_nt : 0;
+        const int fq = n_full > q ? (n_full - 1 - q) / 8 + 1 : 0;
+        const int pq = n_part > q ? (n_part - 1 - q) / 8 + 1 : 0;
         const int i = atomicAdd(&queues[q], 1);
-        if (i < len) {
-          found = (q + 8 * (i / n_nt)) * n_nt + i % n_nt;
+        if (i < (fq + pq) * n_nt) {
+          const int m = i / n_nt, both = min(fq, pq);
+          bool full;
+          int ord;
+          if (m < 2 * both) {
+            full = (m & 1) == 0;
+            ord = m >> 1;
+          } else {
+            full = fq > pq;
+            ord = m - both;
+          }
+          const int mt = full ? q + 8 * ord : n_full + q + 8 * ord;
+          found = mt * n_nt + i % n_nt;
           break;
         }
         q = (q + 1) & 7;

@@ -18,7 +18,7 @@ struct RoutePackParams {
   int32_t* expert_offsets;
   int32_t* sorted_route_ids;
   int32_t* block_expert;
-  int32_t* live;                 // [64]: valid, padded, live blocks, m, M tiles; [8..23] GEMM queues
+  int32_t* live;                 // [64]: valid, padded, live blocks, m, M tiles, full M tiles; [8..23] GEMM queues
   int32_t* route_slot;
   int2* tiles;                   // [cap_blocks] (first block, blocks | expert << 8) or null
   int2* slot_info;               // [cap_routes] (token, router weight bits) or null

@@ -87,7 +87,7 @@ __host__ __device__ inline PackGeom make_pack_geom(int64_t cap, int64_t k, int64
   p.off_offsets = o;      o = align256(o + size_t(E + 1) * 4);
   p.off_sorted = o;       o = align256(o + size_t(p.cap_routes) * 4);
   p.off_block_expert = o; o = align256(o + size_t(p.cap_blocks) * 4);
-  p.off_live = o;         o = align256(o + 64 * 4);  // [0..3] public, [4] M tiles, [8..23] GEMM queues
+  p.off_live = o;         o = align256(o + 64 * 4);  // [0..3] public, [4] M tiles, [5] full ones, [8..23] GEMM queues
   p.off_route_slot = o;   o = align256(o + size_t(routes) * 4);
   // fused-layer extras: M-tile table (first block, block count) and token + weight per slot
   p.off_tiles = o;        o = align256(o + size_t(p.cap_blocks) * 8);

@@ -106,6 +106,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
     tile_carry += ttot;
   }
   const int total_padded = carry;
+  const int full_tiles = tile_carry;
   if (p.tiles) {
     // Partial tiles after all full ones. Thread e reads back the offsets it wrote above.
     for (int base = 0; base < E; base += kPackThreads) {
@@ -128,6 +129,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
     p.live[2] = total_padded / B;
     p.live[3] = int(p.m);
     p.live[4] = tile_carry;
+    p.live[5] = full_tiles;
   }
   if (tid < 16) p.live[8 + tid] = 0;                       // grouped-GEMM work queues: 8 per phase
   for (int64_t s = total_padded + tid; s < p.cap_routes; s += kPackThreads) {

@@ -225,6 +225,27 @@ def test_fused_matches_oracle_scaled(moe, device, name, m, path):
     _check(case, bf16_tensor_to_f64(out), label=f"{name} m={m} {path}")
 
 
+@pytest.mark.parametrize("name,m", [("edge_s", 100), ("prefill_s", 300)])
+def test_gemm_repeat_runs_over_a_dirty_workspace(moe, device, name, m):
+    """The grouped-GEMM pipeline reads every activation stage only after it has landed: repeated
+    runs over a workspace holding large finite garbage all match the oracle (a stage read too
+    early shows up as a wrong intermediate row in some of the runs)."""
+    cfg = SCALED[name]
+    _say(f"gemm repeat {name} m={m}")
+    case = make_case(cfg, m, seed=cfg.index * 7 + m, weights="normal")
+    layer = make_layer(case, device)
+    ref = oracle_out(case)
+    moe.moe_w4a16_set_path("gemm")
+    try:
+        for rep in range(6):
+            layer.workspace.fill_(0x7F)
+            got = bf16_tensor_to_f64(run_layer(layer, case, device))
+            ok, err, bound = M.within_tolerance(got, ref)
+            assert ok, f"{name} m={m} run {rep}: {err} > {bound}"
+    finally:
+        moe.moe_w4a16_set_path("auto")
+
+
 def test_fused_capacity_reuse_one_workspace(moe, device):
     cfg = SCALED["edge_s"]
     case0 = make_case(cfg, 128, seed=41, weights="normal")
