@@ -294,9 +294,11 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   rp.block_expert = reinterpret_cast<int32_t*>(pk + pg.off_block_expert);
   rp.live = reinterpret_cast<int32_t*>(pk + pg.off_live);
   rp.route_slot = reinterpret_cast<int32_t*>(pk + pg.off_route_slot);
-  rp.tiles = reinterpret_cast<int2*>(pk + pg.off_tiles);
+  rp.tiles = decode ? nullptr : reinterpret_cast<int2*>(pk + pg.off_tiles);   // M tiles: grouped GEMM only
   rp.slot_info = reinterpret_cast<int2*>(pk + pg.off_tok_of_slot);
-  const bool convert = !decode && dims->fmt == MOE_FMT_NVFP4_E4M3_K16;
+  // NVFP4 weights run on the f16 MFMA wherever the activations are staged whole: the grouped
+  // GEMM always, the decode path when its rows fit in LDS.
+  const bool convert = dims->fmt == MOE_FMT_NVFP4_E4M3_K16 && (!decode || decode_stages_x(g, m));
   rp.x = x;
   rp.x16 = convert ? reinterpret_cast<uint16_t*>(ws + fg.off_x16) : nullptr;
   rp.xexp = convert ? reinterpret_cast<int32_t*>(ws + fg.off_xexp) : nullptr;
@@ -328,7 +330,9 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   fp.cap_blocks = pg.cap_blocks;
 
   if (events) (void)hipEventRecord(events[0], stream);
-  if (hipError_t e = launch_route_pack(rp, decode ? 0 : cus, stream); e != hipSuccess)
+  // extra route-pack workgroups for the conversion: one wave per row, 16 waves each
+  const int side_blocks = decode ? int((m + 15) / 16) : cus;
+  if (hipError_t e = launch_route_pack(rp, side_blocks, stream); e != hipSuccess)
     return launch_status(e, "route pack launch");
   if (events) (void)hipEventRecord(events[1], stream);
   hipEvent_t* marks = events ? events + 2 : nullptr;

@@ -63,67 +63,18 @@ struct F1Unit {
 template <int FMT, bool STAGED>
 __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p) {
   extern __shared__ __align__(16) uint8_t dyn[];
-  __shared__ f32x4 red[kF1Waves][2][64];
+  // Partial sums of waves 1..3 for the item epilogue, double-buffered by item parity so that
+  // one barrier per item suffices: a wave refills a buffer only after the next item's
+  // barrier, which wave 0 reaches only after it has read that buffer.
+  __shared__ f32x4 red[2][kF1Waves - 1][2][64];
   const PreparedGeom& g = p.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int q = lane >> 4, col = lane & 15;
-  const int H = g.H, hp = int(g.hp);
-  const int xchunks = hp / 8;                                 // 16-byte chunks per staged row
+  const int H = g.H;
+  const int xp = int(p.xs_pitch);                            // elements per staged row
   const int live_blocks = p.live[2];
-  int4* bt = reinterpret_cast<int4*>(dyn);                   // block -> (expert, g13, g2)
-  int* sp = reinterpret_cast<int*>(dyn + p.lds_block_table - kDecodeMaxM * sizeof(int));   // per-token p
-  uint16_t* xs = reinterpret_cast<uint16_t*>(dyn + p.lds_block_table);   // [m][hp], chunk-swizzled
-
-  for (int b = tid; b < live_blocks; b += kF1Threads) {
-    const int e = p.block_expert[b];
-    bt[b] = make_int4(e, __float_as_int(p.g13[e]), __float_as_int(p.g2[e]), 0);
-  }
-  // Activation rows in LDS, zero-padded to hp. Chunk j of row t sits at chunk j ^ (t & 7)
-  // (hp is a multiple of 128, so every group of 8 chunks is complete): lanes reading the
-  // same K of different tokens hit different banks.
-  // NVFP4 runs on the f16 MFMA: E2M1 x E4M3 weights are exact in f16, and each token's bf16
-  // row is rescaled by a power of two 2^-p (exact) so that its largest magnitude lies in
-  // [2^14, 2^15) before the f16 cast; the epilogue multiplies by 2^p again.
-  constexpr bool F16 = STAGED && FMT == FMT_NVFP4;
-  if (STAGED) {
-    for (int c = tid; c < p.m * xchunks; c += kF1Threads) {
-      const int t = c / xchunks, j = c % xchunks;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (j * 8 < H) v = *reinterpret_cast<const u32x4*>(p.x + int64_t(t) * H + j * 8);
-      *reinterpret_cast<u32x4*>(xs + t * hp + ((j ^ (t & 7)) << 3)) = v;
-    }
-  }
-  lds_barrier();
-  if constexpr (F16) {
-    for (int t = wave; t < p.m; t += kF1Waves) {
-      float mx = 0.f;
-      for (int c = lane; c < xchunks; c += 64) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(xs + t * hp + c * 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          mx = fmaxf(mx, fabsf(__uint_as_float(v[i] << 16)));
-          mx = fmaxf(mx, fabsf(__uint_as_float(v[i] & 0xFFFF0000u)));
-        }
-      }
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
-      if (lane == 0) sp[t] = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 15 : 0;
-    }
-    lds_barrier();
-    for (int c = tid; c < p.m * xchunks; c += kF1Threads) {
-      const int t = c / xchunks;
-      const int neg = -sp[t];
-      u32x4* ptr = reinterpret_cast<u32x4*>(xs + t * hp + (c % xchunks) * 8);
-      const u32x4 v = *ptr;
-      f16x2 h[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        h[i] = f16x2{(_Float16)ldexpf(__uint_as_float(v[i] << 16), neg),
-                     (_Float16)ldexpf(__uint_as_float(v[i] & 0xFFFF0000u), neg)};
-      *ptr = __builtin_bit_cast(u32x4, h);
-    }
-    lds_barrier();
-  }
+  uint16_t* xs = reinterpret_cast<uint16_t*>(dyn);           // [m][xp], chunk-swizzled
+  int* sp = reinterpret_cast<int*>(dyn + size_t(p.m) * xp * 2);   // [64] per-token exponent p
 
   const int n_it = int(g.n1_groups / 2);                      // items per block: two row groups
   const int n_items = live_blocks * n_it;
@@ -134,17 +85,38 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
   const int U2 = (U + 1) & ~1;                                // even: units are taken in pairs
   const int kb1 = int(g.kb1);
   const int sc_lane = FMT == FMT_NVFP4 ? ((lane >> 5) * 16 + col) * 16 : col * 16;
+  if (U == 0) return;
+
+  // NVFP4 runs on the f16 MFMA: E2M1 x E4M3 weights are exact in f16, and the route-pack
+  // launch stored each token's row times a power of two 2^-p (exact) with its largest
+  // magnitude in [2^14, 2^15) as f16; the epilogue multiplies by 2^p again.
+  constexpr bool F16 = STAGED && FMT == FMT_NVFP4;
+  if constexpr (STAGED) {
+    // Activation rows into LDS by DMA, zero-padded to xp. Chunk j of row t sits at chunk
+    // j ^ (t & 7) (hp is a multiple of 128, so every group of 8 chunks is complete): lanes
+    // reading the same K of different tokens hit different banks. Lane i of a DMA row writes
+    // LDS chunk 64c + i, so it fetches source chunk (64c + i) ^ (t & 7).
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(F16 ? p.x16 : p.x, uint32_t(p.m * H * 2));
+    const int per_row = xp / 512;
+    for (int n = wave; n < int(p.m) * per_row; n += kF1Waves) {
+      const int t = n / per_row, c = n % per_row;
+      const int j = (64 * c + lane) ^ (t & 7);
+      dma16(xr, reinterpret_cast<const uint8_t*>(xs + t * xp + 512 * c), j * 8 < H ? uint32_t(t * H * 2 + j * 16) : kOutOfRange);
+    }
+    if (F16 && wave == 0) dma4(buffer_rsrc(p.xexp, uint32_t(p.m * 4)), sp, uint32_t(lane * 4));
+  }
 
   // Loads are unconditional so that the wait counters stay exact: units past the end and
   // K blocks past kb1 re-read a valid block (an L2 hit) whose contribution is skipped.
-  // Base addresses are wave-uniform (scalar registers); lanes add a 32-bit offset.
+  // Base addresses are wave-uniform (scalar registers); lanes add a 32-bit offset. The
+  // block's expert comes through the scalar cache, so it waits on no vector load.
   auto issue = [&](int u, F1Unit& r) {
     const int uu = min(u, U - 1);
     const int item = int(blockIdx.x) + (uu / spw) * int(gridDim.x);
     const int sl = min(wave + kF1Waves * (uu % spw), nsl - 1);
     const int blk = item / n_it, it = item % n_it;
     r.info = p.slot_info[blk * kBlockM + col];
-    const int64_t gi = int64_t(uniform(bt[blk].x)) * g.n1_groups + 2 * it;
+    const int64_t gi = int64_t(scalar_load(p.block_expert, blk)) * g.n1_groups + 2 * it;
     const uint8_t* nb0 = p.nib1 + gi * g.kb1 * kFragBytes;
     const uint8_t* nb1 = nb0 + g.kb1 * kFragBytes;
 #pragma unroll
@@ -158,6 +130,14 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
     r.s1 = *reinterpret_cast<const u32x4*>(sg0 + g.sc1_per_group + sc_lane);
   };
 
+  // Two register sets: the next unit's loads stay in flight while this one is computed. The
+  // first two units go out right behind the activation DMA; one wait covers both.
+  F1Unit ra, rb;
+  issue(0, ra);
+  issue(1, rb);
+  if constexpr (STAGED) wait_vmcnt<0>();
+  lds_barrier();
+
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int u, const F1Unit& r) {
     if (u >= U) return;
@@ -167,7 +147,7 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
     const int t = max(tok, 0);                                // padding columns read row 0; masked later
     int xoff[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) xoff[s] = t * hp + (((4 * s + q) ^ (t & 7)) << 3);
+    for (int s = 0; s < 4; ++s) xoff[s] = t * xp + (((4 * s + q) ^ (t & 7)) << 3);
 #pragma unroll
     for (int j = 0; j < kF1Slice; ++j) {
       const int kb = sl * kF1Slice + j;
@@ -196,28 +176,29 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
     }
   };
 
-  auto finish = [&](int u, const F1Unit& r) {
+  auto finish = [&](int u, const int2 info) {
     if (u >= U || u % spw != spw - 1) return;                 // not the item's last slice
-    red[wave][0][lane] = acc0;
-    red[wave][1][lane] = acc1;
-    acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int item = int(blockIdx.x) + (u / spw) * int(gridDim.x);
+    const int blk = item / n_it, it = item % n_it;
+    const int par = (u / spw) & 1;
+    const int e = scalar_load(p.block_expert, blk);
+    float g13 = scalar_load(p.g13, e);
+    const float g2 = scalar_load(p.g2, e);
+    if (wave != 0) {
+      red[par][wave - 1][0][lane] = acc0;
+      red[par][wave - 1][1][lane] = acc1;
+    }
     lds_barrier();
     if (wave == 0) {
-      f32x4 h0 = red[0][0][lane], h1 = red[0][1][lane];
+      f32x4 h0 = acc0, h1 = acc1;
 #pragma unroll
-      for (int w = 1; w < kF1Waves; ++w) {
-        h0 += red[w][0][lane];
-        h1 += red[w][1][lane];
+      for (int w = 0; w < kF1Waves - 1; ++w) {
+        h0 += red[par][w][0][lane];
+        h1 += red[par][w][1][lane];
       }
-      const int item = int(blockIdx.x) + (u / spw) * int(gridDim.x);
-      const int blk = item / n_it, it = item % n_it;
-      const int4 b4 = bt[blk];
-      const int tok = r.info.x;
-      float g13 = __int_as_float(b4.y);
-      const float g2 = __int_as_float(b4.z);
+      const int tok = info.x;
       if constexpr (F16) g13 = ldexpf(g13, tok >= 0 ? sp[tok] : 0);
-      const float rw = (tok >= 0) ? __int_as_float(r.info.y) * g2 : 0.f;
+      const float rw = (tok >= 0) ? __int_as_float(info.y) * g2 : 0.f;
       uint16_t* dst = p.inter + int64_t(blk * kBlockM + col) * g.ip;
       const int r0 = 4 * q;
       if (g.act == ACT_SWIGLU) {
@@ -237,20 +218,21 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
         *reinterpret_cast<uint2*>(dst + 32 * it + 16 + r0) = make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
       }
     }
-    lds_barrier();
+    acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
   };
 
-  // Two register sets: the next unit's loads stay in flight while this one is computed.
-  if (U == 0) return;
-  F1Unit ra, rb;
-  issue(0, ra);
+  // A unit's register set is refilled right after its MFMAs, before the item's epilogue and
+  // its barrier, so the weight stream keeps flowing while waves wait there.
   for (int u = 0; u < U2; u += 2) {
-    issue(u + 1, rb);
     compute(u, ra);
-    finish(u, ra);
+    const int2 ia = ra.info;
     issue(u + 2, ra);
+    finish(u, ia);
     compute(u + 1, rb);
-    finish(u + 1, rb);
+    const int2 ib = rb.info;
+    issue(u + 3, rb);
+    finish(u + 1, ib);
   }
 }
 
@@ -273,11 +255,6 @@ __global__ __launch_bounds__(kF2Threads, 1) void decode_fc2_kernel(FusedParams p
   const int live_blocks = p.live[2];
   int* be = reinterpret_cast<int*>(dyn);                     // block -> expert
   int* stok = be + p.cap_blocks;                             // slot -> token (-1 = padding)
-  for (int b = tid; b < live_blocks; b += kF2Threads) be[b] = p.block_expert[b];
-  for (int s = tid; s < live_blocks * kBlockM; s += kF2Threads) stok[s] = p.slot_info[s].x;
-  for (int i = tid; i < kF2Waves * kDecodeMaxM * 16; i += kF2Threads) (&tacc[0][0][0])[i] = 0.f;
-  lds_barrier();
-
   static_assert(kScaleChunkKB % kF2Slice == 0, "an FC2 unit never straddles a scale chunk");
   const int kb2 = int(g.kb2);
   const int nsl = (kb2 + kF2Slice - 1) / kF2Slice;
@@ -289,10 +266,10 @@ __global__ __launch_bounds__(kF2Threads, 1) void decode_fc2_kernel(FusedParams p
   // Weight loads are unconditional (units past the end re-read the last one, skipped);
   // intermediate rows are loaded only for live route columns, so L2 traffic follows the
   // routes, not the padded blocks.
-  auto issue = [&](int u, F2Unit& r) {
+  auto issue = [&](int u, F2Unit& r, bool prologue) {
     const int unit = wave + min(u, U - 1) * kF2Waves;
     const int blk = unit / nsl, sl = unit % nsl;
-    const int64_t gi = int64_t(uniform(be[blk])) * g.n2_groups + ht;
+    const int64_t gi = int64_t(uniform(prologue ? p.block_expert[blk] : be[blk])) * g.n2_groups + ht;
     const uint8_t* nb = p.nib2 + gi * g.kb2 * kFragBytes;
 #pragma unroll
     for (int j = 0; j < kF2Slice; ++j) {
@@ -303,7 +280,7 @@ __global__ __launch_bounds__(kF2Threads, 1) void decode_fc2_kernel(FusedParams p
     r.s = *reinterpret_cast<const uint2*>(p.sc2 + gi * g.sc2_per_group + int64_t(kb0 / kScaleChunkKB) * g.sc_chunk_bytes +
                                           sc_lane + (kb0 % kScaleChunkKB) * 4);
     const int slot = blk * kBlockM + col;
-    const bool valid = stok[slot] >= 0;
+    const bool valid = (prologue ? p.slot_info[slot].x : stok[slot]) >= 0;
     const uint16_t* irow = p.inter + int64_t(slot) * g.ip + 8 * q;
 #pragma unroll
     for (int j = 0; j < kF2Slice; ++j) {
@@ -312,6 +289,19 @@ __global__ __launch_bounds__(kF2Threads, 1) void decode_fc2_kernel(FusedParams p
       for (int s = 0; s < 4; ++s) r.b[j][s] = valid ? load_bf16x8(irow + kb * kKBlock + 32 * s) : zero_bf16x8();
     }
   };
+  // The first two units' loads go out before the table staging below. Two register sets:
+  // the next unit's loads stay in flight while this one is computed.
+  F2Unit ra, rb;
+  if (U > 0) {
+    issue(0, ra, true);
+    issue(1, rb, true);
+  }
+
+  for (int b = tid; b < live_blocks; b += kF2Threads) be[b] = p.block_expert[b];
+  for (int s = tid; s < live_blocks * kBlockM; s += kF2Threads) stok[s] = p.slot_info[s].x;
+  for (int i = tid; i < kF2Waves * kDecodeMaxM * 16; i += kF2Threads) (&tacc[0][0][0])[i] = 0.f;
+  lds_barrier();
+
   auto compute = [&](int u, const F2Unit& r) {
     if (u >= U) return;
     const int unit = wave + u * kF2Waves;
@@ -333,16 +323,11 @@ __global__ __launch_bounds__(kF2Threads, 1) void decode_fc2_kernel(FusedParams p
     }
   };
 
-  // Two register sets: the next unit's loads stay in flight while this one is computed.
-  if (U > 0) {
-    F2Unit ra, rb;
-    issue(0, ra);
-    for (int u = 0; u < U2; u += 2) {
-      issue(u + 1, rb);
-      compute(u, ra);
-      issue(u + 2, ra);
-      compute(u + 1, rb);
-    }
+  for (int u = 0; u < U2; u += 2) {
+    compute(u, ra);
+    issue(u + 2, ra, false);
+    compute(u + 1, rb);
+    issue(u + 3, rb, false);
   }
   lds_barrier();
   // Sum the waves in a fixed order and store out[t, 16*ht .. 16*ht + 15] (zero for tokens
@@ -368,24 +353,21 @@ hipError_t allow_lds(K kernel, int bytes) {
 template <int FMT>
 hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t stream, hipEvent_t* marks) {
   static const hipError_t lds_ok = [] {
-    // dynamic LDS: block table (<= 1024 blocks at capacity 16) + staged rows / slot tokens
-    hipError_t e = allow_lds(&decode_fc1_kernel<FMT, true>, kDecodeStageBytes + 32768);
-    if (e == hipSuccess) e = allow_lds(&decode_fc1_kernel<FMT, false>, 32768);
+    // dynamic LDS: FC1 staged rows + exponents; FC2 block table + slot tokens
+    hipError_t e = allow_lds(&decode_fc1_kernel<FMT, true>, kDecodeStageBytes + 256);
     if (e == hipSuccess) e = allow_lds(&decode_fc2_kernel<FMT>, 98304);
     return e;
   }();
   if (lds_ok != hipSuccess) return lds_ok;
   FusedParams p = p0;
   const PreparedGeom& g = p.g;
-  const size_t table = align256(size_t(p.cap_blocks) * sizeof(int4) + kDecodeMaxM * sizeof(int));
-  p.lds_block_table = int64_t(table);
+  p.xs_pitch = decode_x_pitch(g);
   const int64_t items = p.cap_blocks * (g.n1_groups / 2);
   const int64_t grid1 = max(int64_t(1), min(items, int64_t(num_cus) * 2));
-  const size_t xs_bytes = size_t(p.m) * g.hp * 2;
-  if (xs_bytes <= size_t(kDecodeStageBytes))
-    hipLaunchKernelGGL((decode_fc1_kernel<FMT, true>), dim3(grid1), dim3(kF1Threads), table + xs_bytes, stream, p);
+  if (decode_stages_x(g, p.m))
+    hipLaunchKernelGGL((decode_fc1_kernel<FMT, true>), dim3(grid1), dim3(kF1Threads), size_t(p.m) * p.xs_pitch * 2 + 256, stream, p);
   else
-    hipLaunchKernelGGL((decode_fc1_kernel<FMT, false>), dim3(grid1), dim3(kF1Threads), table, stream, p);
+    hipLaunchKernelGGL((decode_fc1_kernel<FMT, false>), dim3(grid1), dim3(kF1Threads), 0, stream, p);
   if (marks) (void)hipEventRecord(marks[0], stream);
   const size_t lds2 = size_t(p.cap_blocks) * 4 + size_t(p.cap_blocks) * kBlockM * 4;
   hipLaunchKernelGGL((decode_fc2_kernel<FMT>), dim3(g.n2_groups), dim3(kF2Threads), lds2, stream, p);

@@ -132,6 +132,48 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
 // Workgroup barrier that orders LDS only. __syncthreads() also waits for every outstanding
 // global load of the wave (gfx9 counts loads and stores in one vmcnt), which would drain
 // the weight prefetch; LDS hand-offs between waves need only lgkmcnt.
+constexpr uint32_t kOutOfRange = 0x80000000u;           // set in a buffer offset: past every num_records, loads 0
+
+// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14; expcnt and lgkmcnt at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// A pointer the compiler cannot prove wave-uniform, moved to scalar registers (it is uniform).
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+}
+
+// 16 bytes per lane from a buffer into LDS at lds_dst + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const uint8_t* lds_dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, int(voff), 0, 0, 0);
+}
+
+// 4 bytes per lane from a buffer into LDS at lds_dst + 4 * lane.
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const void* lds_dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 4, int(voff), 0, 0, 0);
+}
+
+// Buffer resource over `bytes` bytes at p (raw, no stride; loads past the end return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(p), 0, int(bytes), 0x00020000);
+}
+
+// Load through the scalar cache: `i` must be wave-uniform and the data must not change
+// during the launch (it was written by an earlier launch).
+__device__ __forceinline__ int32_t scalar_load(const int32_t* p, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+__device__ __forceinline__ float scalar_load(const float* p, int i) {
+  return ((const __attribute__((address_space(4))) float*)p)[i];
+}
+
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();

@@ -32,7 +32,6 @@ namespace {
 
 constexpr int kGemmThreads = 512;                       // 8 waves, two per SIMD
 constexpr int kGemmWaves = kGemmThreads / 64;
-constexpr uint32_t kOutOfRange = 0x80000000u;           // set in a buffer offset: past every num_records, loads 0
 constexpr int kRowBytes = kKBlock * 2;                  // one activation row of a K block: 256 B
 constexpr int kBlockBytes = kBlockM * kRowBytes;        // one route block of a K block: 4 KiB
 constexpr int kLdsBytes = 131072;                       // the activation stage ring
@@ -53,14 +52,6 @@ struct Plan {
   static_assert(XD <= 2 * FR, "the stage wait relies on at least as many register loads as LDS loads");
 };
 
-// s_waitcnt with only the vector-memory counter bounded (gfx9 encoding: vmcnt in bits 3:0
-// and 15:14; expcnt and lgkmcnt at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // Workgroup barrier for the stage ring. A release fence would make every wave wait for all of
 // its loads into LDS, including the stages still meant to be in flight; instead each wave
 // waits explicitly for the stage it needs (wait_vmcnt) and for its own LDS reads (lgkmcnt 0,
@@ -70,19 +61,6 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maxima
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// A pointer the compiler cannot prove wave-uniform, moved to scalar registers (it is uniform).
-__device__ __forceinline__ void* uniform_ptr(const void* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
-  return reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
-}
-
-// 16 bytes per lane from a buffer into LDS at lds_dst + 16 * lane.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const uint8_t* lds_dst, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, int(voff), 0, 0, 0);
 }
 
 // Per-launch constants shared by every item of a workgroup.
@@ -462,13 +440,17 @@ hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hi
   if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   if (marks) (void)hipEventRecord(marks[1], stream);
+  launch_combine(p, stream);
+  if (marks) (void)hipEventRecord(marks[2], stream);
+  return hipGetLastError();
+}
+
+void launch_combine(const FusedParams& p, hipStream_t stream) {
   const int64_t n = p.m * p.g.H / 4;
   int64_t cb = (n + 255) / 256;
   if (cb < 1) cb = 1;
   if (cb > 8192) cb = 8192;
   hipLaunchKernelGGL(combine_kernel, dim3(cb), dim3(256), 0, stream, p.y, p.route_slot, p.out, p.m, p.topk, int64_t(p.g.H));
-  if (marks) (void)hipEventRecord(marks[2], stream);
-  return hipGetLastError();
 }
 
 }  // namespace moe

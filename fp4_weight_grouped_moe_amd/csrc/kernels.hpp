@@ -61,11 +61,11 @@ struct FusedParams {
   const int2* slot_info;
   const int32_t* route_slot;      // [m * topk] packed slot of each route or -1
   uint16_t* inter;               // bf16 [cap_routes, ip]
-  const uint16_t* x16;           // f16 [m, H] scaled activations (grouped GEMM, NVFP4)
+  const uint16_t* x16;           // f16 [m, H] scaled activations (NVFP4 f16 MFMA route)
   const int32_t* xexp;           // [m] their per-token exponents
   float* y;                      // fp32 [m * topk, H] weighted FC2 rows per route (grouped GEMM)
   int64_t cap_blocks;
-  int64_t lds_block_table;       // decode FC1: bytes of LDS before the staged activations
+  int64_t xs_pitch;              // decode FC1: elements per staged activation row in LDS
 };
 
 size_t route_pack_lds_bytes(int num_experts);
@@ -76,5 +76,7 @@ hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
 // combine (the decode path records its last mark right after FC2).
 hipError_t launch_decode(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks);
 hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks);
+// out = bf16 of the sum of each token's valid route rows y[route] (route order).
+void launch_combine(const FusedParams& p, hipStream_t stream);
 
 }  // namespace moe

@@ -99,6 +99,12 @@ __host__ __device__ inline PackGeom make_pack_geom(int64_t cap, int64_t k, int64
 constexpr int kDecodeMaxM = 16;          // token columns of the decode path
 constexpr int kDecodeStageBytes = 65536; // LDS for the decode kernels' staged activation rows
 
+// Decode FC1 keeps the activation rows in LDS when they fit, at a pitch of hp rounded up to
+// 512 elements (whole 1 KiB rows of LDS DMA). With NVFP4 weights the staged rows are the f16
+// copy made by the route-pack launch.
+inline int64_t decode_x_pitch(const PreparedGeom& g) { return (g.hp + 511) / 512 * 512; }
+inline bool decode_stages_x(const PreparedGeom& g, int64_t m) { return m * decode_x_pitch(g) * 2 <= kDecodeStageBytes; }
+
 // Fused-layer workspace: route pack (block 16), bf16 intermediate rows per packed slot,
 // and for the grouped-GEMM path the f16 copy of the activations with per-token exponents
 // (NVFP4) and the fp32 FC2 row of every route, summed over top-k by the combine pass.

@@ -1,12 +1,13 @@
 // Route packing on gfx950: group token x expert routes by local expert into a padded,
 // power-of-two-capacity workspace (FlashInfer PR 4255, Description: shape-stable route
 // packing; Tests: expert_map and invalid expert ids). One 1024-thread workgroup does the
-// whole pack; for the grouped-GEMM path with NVFP4 weights every other workgroup of the
-// same launch converts the activation rows to f16 (exact up to f16 subnormals, below
+// whole pack; for the NVFP4 weights' f16 MFMA route every other workgroup of the same
+// launch converts the activation rows to f16 (exact up to f16 subnormals, below
 // 2^-38 of the row maximum) times a per-token power of two, so that no separate launch is
 // needed.
 #include <hip/hip_runtime.h>
 
+#include "device.hpp"
 #include "kernels.hpp"
 #include "layout.hpp"
 
@@ -16,6 +17,8 @@ namespace {
 
 constexpr int kPackThreads = 1024;
 constexpr int kPackWaves = kPackThreads / 64;
+constexpr int kValidSlot = 36;                 // scan scratch entries 0 .. 2 kPackWaves + 1 are the scans'
+constexpr int kRowRegs = 8;                    // 16-byte chunks per lane per batch of the row conversion
 
 __device__ __forceinline__ int local_expert(const RoutePackParams& p, int64_t r) {
   if (r >= p.num_routes) return -1;
@@ -54,19 +57,52 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int* total) {
   return r;
 }
 
+// Exclusive scans of two ints per thread at once (one set of barriers); wave_tot needs
+// 2 * (kPackWaves + 1) ints.
+__device__ int2 block_exclusive_scan2(int v0, int v1, int* wave_tot, int* total0, int* total1) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x0 = v0, x1 = v1;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y0 = __shfl_up(x0, d, 64), y1 = __shfl_up(x1, d, 64);
+    if (lane >= d) { x0 += y0; x1 += y1; }
+  }
+  if (lane == 63) { wave_tot[w] = x0; wave_tot[kPackWaves + 1 + w] = x1; }
+  __syncthreads();
+  if (w == 0) {
+    const int t0 = lane < kPackWaves ? wave_tot[lane] : 0;
+    const int t1 = lane < kPackWaves ? wave_tot[kPackWaves + 1 + lane] : 0;
+    int s0 = t0, s1 = t1;
+#pragma unroll
+    for (int d = 1; d < kPackWaves; d <<= 1) {
+      const int y0 = __shfl_up(s0, d, 64), y1 = __shfl_up(s1, d, 64);
+      if (lane >= d) { s0 += y0; s1 += y1; }
+    }
+    if (lane < kPackWaves) { wave_tot[lane] = s0 - t0; wave_tot[kPackWaves + 1 + lane] = s1 - t1; }
+    if (lane == kPackWaves - 1) { wave_tot[kPackWaves] = s0; wave_tot[2 * kPackWaves + 1] = s1; }
+  }
+  __syncthreads();
+  const int2 r = make_int2(x0 - v0 + wave_tot[w], x1 - v1 + wave_tot[kPackWaves + 1 + w]);
+  *total0 = wave_tot[kPackWaves];
+  *total1 = wave_tot[2 * kPackWaves + 1];
+  __syncthreads();
+  return r;
+}
+
 __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.num_experts, B = p.block_m;
   int* cnt = reinterpret_cast<int*>(smem);                 // [E] counts, then running slot
-  int* wave_tot = cnt + E;                                 // [32] scan scratch; [20] = valid routes
-  uint8_t* wcnt = reinterpret_cast<uint8_t*>(wave_tot + 32);  // [kPackWaves][E] per-wave counts
+  int* wave_tot = cnt + E;                                 // [40] scan scratch; [kValidSlot] = valid routes
+  int* ecnt = wave_tot + 40;                               // [E] counts (kept for the tile table)
+  uint8_t* wcnt = reinterpret_cast<uint8_t*>(ecnt + E);    // [kPackWaves][E] per-wave counts
 
   // The first chunk's local id and router weight stay in registers for the scatter, so
   // small batches read topk_ids / expert_map / topk_weights from memory only once.
   const int l_first = local_expert(p, tid);
   const float w_first = (p.topk_weights && tid < p.num_routes) ? p.topk_weights[tid] : 0.f;
   for (int e = tid; e < E; e += kPackThreads) cnt[e] = 0;
-  if (tid == 0) wave_tot[kPackWaves + 4] = 0;
+  if (tid == 0) wave_tot[kValidSlot] = 0;
   for (int i = tid; i < kPackWaves * E; i += kPackThreads) wcnt[i] = 0;
   __syncthreads();
   if (l_first >= 0) atomicAdd(&cnt[l_first], 1);
@@ -86,8 +122,8 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
     int padded = (c + B - 1) / B * B;
     int nfull = padded / B / kTileBlocks;
     int tot, ttot;
-    int off = block_exclusive_scan(padded, wave_tot, &tot) + carry;
-    int toff = block_exclusive_scan(nfull, wave_tot, &ttot) + tile_carry;
+    const int2 sc2 = block_exclusive_scan2(padded, nfull, wave_tot, &tot, &ttot);
+    const int off = sc2.x + carry, toff = sc2.y + tile_carry;
     if (e < E) {
       p.expert_counts[e] = c;
       p.expert_offsets[e] = off;
@@ -101,6 +137,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
           p.tiles[toff + t] = make_int2(off / B + t * kTileBlocks, kTileBlocks | (e << 8));
       }
       cnt[e] = off;                                        // running slot of expert e
+      ecnt[e] = c;
     }
     carry += tot;
     tile_carry += ttot;
@@ -108,13 +145,13 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   const int total_padded = carry;
   const int full_tiles = tile_carry;
   if (p.tiles) {
-    // Partial tiles after all full ones. Thread e reads back the offsets it wrote above.
+    // Partial tiles after all full ones (counts and offsets kept in LDS by the pass above).
     for (int base = 0; base < E; base += kPackThreads) {
       int e = base + tid;
       int blocks = 0, off = 0;
       if (e < E) {
-        off = p.expert_offsets[e];
-        blocks = (p.expert_counts[e] + B - 1) / B;
+        off = cnt[e];
+        blocks = (ecnt[e] + B - 1) / B;
       }
       int rem = blocks % kTileBlocks;
       int ttot;
@@ -143,22 +180,23 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   // Stable scatter, 1024 routes per chunk: rank inside the wave by matching equal expert
   // ids, then add the counts of lower waves of the chunk and the running slot.
   int valid_total = 0;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int64_t base = 0; base < p.num_routes; base += kPackThreads) {
     const int64_t r = base + tid;
     const int l = base == 0 ? l_first : local_expert(p, r);
-    int rank = 0;
-    uint64_t todo = __ballot(l >= 0);
-    valid_total += __popcll(todo);
-    while (todo) {
-      const int leader = __ffsll((long long)todo) - 1;
-      const int ev = __builtin_amdgcn_readlane(l, leader);
-      const uint64_t same = __ballot(l == ev);
-      if (l == ev) {
-        rank = __popcll(same & lt_mask);
-        if (lane == leader) wcnt[wave * E + ev] = (uint8_t)__popcll(same);
+    // Stable rank among the wave's earlier lanes with the same expert, and the wave's count
+    // per expert (written by the expert's first lane): one pass over the 64 lanes' ids.
+    int rank = 0, same = 0;
+    const uint64_t valid_mask = __ballot(l >= 0);
+    valid_total += __popcll(valid_mask);
+    if (valid_mask) {
+      const int nl = 64 - __builtin_clzll(valid_mask);          // lanes at and above the last valid one hold no route
+      for (int j = 0; j < nl; ++j) {
+        const int lj = __builtin_amdgcn_readlane(l, j);
+        const int eq = lj == l;
+        same += eq;
+        rank += eq & (j < lane);
       }
-      todo &= ~same;
+      if (l >= 0 && rank == 0) wcnt[wave * E + l] = (uint8_t)same;
     }
     __syncthreads();
     if (l >= 0) {
@@ -187,9 +225,9 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
     }
   }
   // valid_total is per wave (ballots are wave-wide); lane 0 of each wave adds its share.
-  if (lane == 0) atomicAdd(&wave_tot[kPackWaves + 4], valid_total);
+  if (lane == 0) atomicAdd(&wave_tot[kValidSlot], valid_total);
   __syncthreads();
-  if (tid == 0) p.live[0] = wave_tot[kPackWaves + 4];
+  if (tid == 0) p.live[0] = wave_tot[kValidSlot];
 }
 
 }  // namespace
@@ -204,42 +242,74 @@ __global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParam
   // then the scaled f16 row (hidden % 8 == 0: 16-byte chunks).
   const int lane = threadIdx.x & 63;
   const int64_t waves = int64_t(gridDim.x - 1) * (blockDim.x / 64);
-  const int64_t chunks = p.hidden / 8;
-  for (int64_t t = int64_t(blockIdx.x - 1) * (blockDim.x / 64) + (threadIdx.x >> 6); t < p.m; t += waves) {
-    const uint4* row = reinterpret_cast<const uint4*>(p.x + t * p.hidden);
-    float amax = 0.f;
-    for (int64_t c = lane; c < chunks; c += 64) {
-      const uint4 v = row[c];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[i] << 16)), fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
+  const int chunks = int(p.hidden / 8);
+  auto pexp_of = [](float amax) {
     int e = 0;
     if (amax > 0.f && amax <= 3.4e38f) (void)frexpf(amax, &e);   // amax = f * 2^e, f in [0.5, 1)
-    const int pexp = amax > 0.f && amax <= 3.4e38f ? e - 15 : 0;
-    const float inv = ldexpf(1.f, -pexp);
-    uint4* dst = reinterpret_cast<uint4*>(p.x16 + t * p.hidden);
-    for (int64_t c = lane; c < chunks; c += 64) {
-      const uint4 v = row[c];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t o[4];
+    return amax > 0.f && amax <= 3.4e38f ? e - 15 : 0;
+  };
+  auto row_max = [&](float amax) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const _Float16 lo = (_Float16)(__uint_as_float(w[i] << 16) * inv);
-        const _Float16 hi = (_Float16)(__uint_as_float(w[i] & 0xFFFF0000u) * inv);
-        o[i] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+    for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
+    return amax;
+  };
+  auto chunk_max = [](const u32x4 v, float amax) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(v[i] << 16)), fabsf(__uint_as_float(v[i] & 0xFFFF0000u))));
+    return amax;
+  };
+  auto to_f16 = [](const u32x4 v, float inv) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 lo = (_Float16)(__uint_as_float(v[i] << 16) * inv);
+      const _Float16 hi = (_Float16)(__uint_as_float(v[i] & 0xFFFF0000u) * inv);
+      o[i] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+    }
+    return o;
+  };
+  for (int64_t t = int64_t(blockIdx.x - 1) * (blockDim.x / 64) + (threadIdx.x >> 6); t < p.m; t += waves) {
+    // Row buffers: loads past the row return 0 and stores past it are dropped.
+    const __amdgpu_buffer_rsrc_t src = buffer_rsrc(p.x + t * p.hidden, uint32_t(p.hidden * 2));
+    const __amdgpu_buffer_rsrc_t dst = buffer_rsrc(p.x16 + t * p.hidden, uint32_t(p.hidden * 2));
+    // Batches of kRowRegs chunks per lane, all loads of a batch in flight together; a row of
+    // one batch stays in registers, longer rows are read a second time for the conversion.
+    u32x4 v[kRowRegs];
+#pragma unroll
+    for (int i = 0; i < kRowRegs; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(src, (lane + 64 * i) * 16, 0, 0);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < kRowRegs; ++i) amax = chunk_max(v[i], amax);
+    for (int base = 64 * kRowRegs; base < chunks; base += 64 * kRowRegs) {
+      u32x4 w[kRowRegs];
+#pragma unroll
+      for (int i = 0; i < kRowRegs; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b128(src, (base + lane + 64 * i) * 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < kRowRegs; ++i) amax = chunk_max(w[i], amax);
+    }
+    const int pexp = pexp_of(row_max(amax));
+    const float inv = ldexpf(1.f, -pexp);
+    if (chunks <= 64 * kRowRegs) {
+#pragma unroll
+      for (int i = 0; i < kRowRegs; ++i)
+        if (lane + 64 * i < chunks) __builtin_amdgcn_raw_buffer_store_b128(to_f16(v[i], inv), dst, (lane + 64 * i) * 16, 0, 0);
+    } else {
+      for (int base = 0; base < chunks; base += 64 * kRowRegs) {
+        u32x4 w[kRowRegs];
+#pragma unroll
+        for (int i = 0; i < kRowRegs; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b128(src, (base + lane + 64 * i) * 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kRowRegs; ++i)
+          if (base + lane + 64 * i < chunks) __builtin_amdgcn_raw_buffer_store_b128(to_f16(w[i], inv), dst, (base + lane + 64 * i) * 16, 0, 0);
       }
-      dst[c] = make_uint4(o[0], o[1], o[2], o[3]);
     }
     if (lane == 0) p.xexp[t] = pexp;
   }
 }
 
 size_t route_pack_lds_bytes(int num_experts) {
-  return size_t(num_experts) * 4 + 32 * 4 + size_t(kPackWaves) * num_experts + 16;
+  return size_t(num_experts) * 8 + 40 * 4 + size_t(kPackWaves) * num_experts + 16;
 }
 
 hipError_t launch_route_pack(const RoutePackParams& p, int side_blocks, hipStream_t stream) {
