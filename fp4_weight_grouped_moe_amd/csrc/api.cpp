@@ -327,6 +327,7 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   fp.x16 = rp.x16;
   fp.xexp = rp.xexp;
   fp.y = reinterpret_cast<float*>(ws + fg.off_y);
+  fp.part = reinterpret_cast<float*>(ws + fg.off_part);
   fp.cap_blocks = pg.cap_blocks;
 
   if (events) (void)hipEventRecord(events[0], stream);

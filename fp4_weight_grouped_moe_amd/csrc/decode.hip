@@ -345,6 +345,199 @@ __global__ __launch_bounds__(kF2Threads, 1) void decode_fc2_kernel(FusedParams p
   }
 }
 
+// ----------------------------------------------------------------------------- FC2, K split
+//
+// Workgroup (G, z) owns RG row groups (16 RG hidden rows) and K blocks 2z, 2z + 1 of the
+// intermediate for every route block. That K slice of every valid route's intermediate row
+// is staged in LDS once (by DMA, row index = route id), so each LDS read of an MFMA B
+// fragment feeds RG MFMAs and the weight stream carries no other loads. Units are route
+// blocks (RG row groups x 2 K blocks = 2 RG KiB of nibbles), dealt to the 8 waves in turn;
+// a unit's route results are added into per-wave, per-token LDS sums. The workgroup's
+// fixed-order sum over waves is one fp32 partial per (K split, token, hidden row), and the
+// combine pass adds the K splits in order: deterministic, no global atomics.
+
+constexpr int kF3Threads = 512;
+constexpr int kF3Waves = kF3Threads / 64;
+constexpr int kF3KB = 2;             // K blocks per workgroup
+constexpr int kF3RowGroups = 2;      // row groups per workgroup
+constexpr int kF3MaxLds = 81920;     // two workgroups per CU
+constexpr int kF3RowBytes = kF3KB * kKBlock * 2;   // staged bytes per route row
+
+template <int RG>
+struct F3Unit {
+  u32x4 q[RG][kF3KB];                // 1 KiB fragment blocks: row group, K block
+  uint32_t s[RG][kF3KB];             // their scale dwords
+};
+
+__host__ __device__ inline size_t f3_rows_bytes(int64_t routes) { return (size_t(routes) * kF3RowBytes + 1023) / 1024 * 1024; }
+__host__ __device__ inline size_t f3_table_bytes(int64_t cap_blocks) { return (size_t(cap_blocks) * kBlockM * 4 + 255) / 256 * 256; }
+__host__ __device__ inline size_t f3_exp_bytes(int64_t routes) { return (size_t(routes) * 4 + 15) / 16 * 16; }
+template <int RG>
+__host__ __device__ inline size_t f3_lds_bytes(int64_t m, int64_t topk, int64_t cap_blocks) {
+  return f3_rows_bytes(m * topk) + f3_table_bytes(cap_blocks) + f3_exp_bytes(m * topk) + size_t(kF3Waves) * m * 16 * RG * 4;
+}
+
+template <int FMT, int RG>
+__global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedParams p) {
+  extern __shared__ __align__(16) uint8_t dyn[];
+  const PreparedGeom& g = p.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
+  const int q = lane >> 4, col = lane & 15;
+  const int nb = p.live[2];
+  const int m = int(p.m), topk = p.topk, routes = m * topk;
+  const int kb2 = int(g.kb2), groups = int(g.n2_groups);
+  const int G = blockIdx.x, kq0 = int(blockIdx.y) * kF3KB;
+  uint8_t* bs = dyn;                                                        // [routes][kF3RowBytes]
+  int* sroute = reinterpret_cast<int*>(dyn + f3_rows_bytes(routes));       // [nb * 16] slot -> route
+  int* sexp = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(sroute) + f3_table_bytes(p.cap_blocks));    // [routes] f16 exponents
+  float* tacc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sexp) + f3_exp_bytes(routes));          // [waves][m][16 RG]
+  const int U = nb > wave ? (nb - wave + kF3Waves - 1) / kF3Waves : 0;
+  const int U2 = (U + 1) & ~1;
+  const int sc_lane = FMT == FMT_NVFP4 ? ((lane >> 5) * 16 + col) * 16 : col * 16;
+
+  // Staging: the slot -> route table and each route's K slice by DMA (dropped routes, the
+  // table's tail and K blocks past kb2 read as zeros).
+  for (int i = tid; i < kF3Waves * m * 16 * RG; i += kF3Threads) tacc[i] = 0.f;
+  const __amdgpu_buffer_rsrc_t tr = buffer_rsrc(p.sorted_route_ids, uint32_t(nb * kBlockM * 4));
+  for (int n = wave; n * 64 < nb * kBlockM; n += kF3Waves) dma4(tr, sroute + 64 * n, uint32_t((64 * n + lane) * 4));
+  const __amdgpu_buffer_rsrc_t ir = buffer_rsrc(p.inter, uint32_t(p.cap_blocks * kBlockM * g.ip * 2));
+  for (int n = wave; n * 1024 < routes * kF3RowBytes; n += kF3Waves) {
+    const int L = n * 1024 + lane * 16;
+    const int r = L / kF3RowBytes, o = L % kF3RowBytes;
+    const int slot = r < routes ? p.route_slot[r] : -1;
+    const bool ok = slot >= 0 && kq0 + o / (kKBlock * 2) < kb2;
+    dma16(ir, bs + n * 1024, ok ? uint32_t(slot * g.ip * 2 + kq0 * kKBlock * 2 + o) : kOutOfRange);
+  }
+
+  // Loads are unconditional so that the wait counters stay exact: units past the end re-read
+  // the last unit, row groups past the end the last group, K blocks past kb2 the last block;
+  // none of these is used.
+  auto issue = [&](int u, F3Unit<RG>& r) {
+    const int blk = wave + min(u, U - 1) * kF3Waves;
+    const int64_t e = scalar_load(p.block_expert, blk);
+#pragma unroll
+    for (int rr = 0; rr < RG; ++rr) {
+      const int64_t gi = e * groups + min(G * RG + rr, groups - 1);
+      const uint8_t* nbp = p.nib2 + gi * kb2 * kFragBytes;
+#pragma unroll
+      for (int j = 0; j < kF3KB; ++j)
+        r.q[rr][j] = *reinterpret_cast<const u32x4*>(nbp + int64_t(min(kq0 + j, kb2 - 1)) * kFragBytes + lane * 16);
+      const uint8_t* sp = p.sc2 + gi * g.sc2_per_group + int64_t(kq0 / kScaleChunkKB) * g.sc_chunk_bytes + sc_lane + (kq0 % kScaleChunkKB) * 4;
+      if constexpr (kF3KB == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sp);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r.s[rr][j] = v[j];
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(sp);
+        r.s[rr][0] = v.x;
+        r.s[rr][1] = v.y;
+      }
+    }
+  };
+  static_assert(kScaleChunkKB % kF3KB == 0 && (kF3KB == 2 || kF3KB == 4), "a workgroup's K blocks never straddle a scale chunk");
+
+  F3Unit<RG> ra, rb;
+  if (U > 0) {
+    issue(0, ra);
+    issue(1, rb);
+  }
+  wait_vmcnt<0>();
+  lds_barrier();
+
+  // NVFP4 runs on the f16 MFMA: E2M1 x E4M3 weights are exact in f16, and each staged route
+  // row is rescaled in place by a power of two 2^-p (exact) with its largest magnitude in
+  // [2^14, 2^15) before the f16 cast; the unit results are multiplied by 2^p again. The
+  // exponent is per (route, K split), and the K splits meet only in fp32 sums.
+  constexpr bool F16 = FMT == FMT_NVFP4;
+  if constexpr (F16) {
+    for (int r = wave; r < routes; r += kF3Waves) {
+      uint32_t* rw = reinterpret_cast<uint32_t*>(bs + r * kF3RowBytes) + lane * kF3KB;
+      uint32_t v[kF3KB];
+      float mx = 0.f;
+#pragma unroll
+      for (int d = 0; d < kF3KB; ++d) {
+        v[d] = rw[d];
+        mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(v[d] << 16)), fabsf(__uint_as_float(v[d] & 0xFFFF0000u))));
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+      const int pe = (mx > 0.f && mx <= 3.4e38f) ? __builtin_amdgcn_frexp_expf(mx) - 15 : 0;
+#pragma unroll
+      for (int d = 0; d < kF3KB; ++d) {
+        const f16x2 h = f16x2{(_Float16)ldexpf(__uint_as_float(v[d] << 16), -pe), (_Float16)ldexpf(__uint_as_float(v[d] & 0xFFFF0000u), -pe)};
+        rw[d] = __builtin_bit_cast(uint32_t, h);
+      }
+      if (lane == 0) sexp[r] = pe;
+    }
+    lds_barrier();
+  }
+
+  auto compute = [&](int u, const F3Unit<RG>& r) {
+    if (u >= U) return;
+    const int blk = wave + u * kF3Waves;
+    const int route = sroute[blk * kBlockM + col];
+    const uint8_t* brow = bs + max(route, 0) * kF3RowBytes + q * 16;
+    f32x4 acc[RG];
+#pragma unroll
+    for (int rr = 0; rr < RG; ++rr) acc[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < kF3KB; ++j) {
+      if (kq0 + j < kb2) {
+        float sc[RG][4];
+#pragma unroll
+        for (int rr = 0; rr < RG; ++rr) decode_scales<FMT>(r.s[rr][j], sc[rr]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if constexpr (F16) {
+            const f16x8 b = route >= 0 ? *reinterpret_cast<const f16x8*>(brow + j * kKBlock * 2 + s * 64) : zero_f16x8();
+#pragma unroll
+            for (int rr = 0; rr < RG; ++rr) acc[rr] = mfma16h(dq8_nv_f16(r.q[rr][j][s], split_nv_scale(sc[rr][s])), b, acc[rr]);
+          } else {
+            const bf16x8 b = route >= 0 ? *reinterpret_cast<const bf16x8*>(brow + j * kKBlock * 2 + s * 64) : zero_bf16x8();
+#pragma unroll
+            for (int rr = 0; rr < RG; ++rr) acc[rr] = mfma16(dq8<FMT>(r.q[rr][j][s], sc[rr][s]), b, acc[rr]);
+          }
+        }
+      }
+    }
+    if (route >= 0) {
+      float* ta = tacc + (wave * m + route / topk) * (16 * RG) + 4 * q;
+      const int pe = F16 ? sexp[route] : 0;
+#pragma unroll
+      for (int rr = 0; rr < RG; ++rr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) atomicAdd(ta + 16 * rr + i, F16 ? ldexpf(acc[rr][i], pe) : acc[rr][i]);
+    }
+  };
+
+  for (int u = 0; u < U2; u += 2) {
+    compute(u, ra);
+    issue(u + 2, ra);
+    compute(u + 1, rb);
+    issue(u + 3, rb);
+  }
+  lds_barrier();
+  // Fixed-order sum over the waves: the partial of K split blockIdx.y for rows of this group.
+  for (int i = tid; i < m * 16 * RG; i += kF3Threads) {
+    const int t = i / (16 * RG), row = i % (16 * RG);
+    const int64_t h = int64_t(G) * 16 * RG + row;
+    float sum = 0.f;
+    for (int w = 0; w < kF3Waves; ++w) sum += tacc[(w * m + t) * (16 * RG) + row];
+    if (h < g.H) p.part[(int64_t(blockIdx.y) * m + t) * g.H + h] = sum;
+  }
+}
+
+// out[t, h] = bf16 of the sum of the K-split partials in split order.
+__global__ void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ out, int64_t m, int64_t H, int nsplit) {
+  const int64_t n4 = m * H / 4;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t e = i * 4;
+    f32x4 s = *reinterpret_cast<const f32x4*>(part + e);
+    for (int z = 1; z < nsplit; ++z) s += *reinterpret_cast<const f32x4*>(part + int64_t(z) * m * H + e);
+    *reinterpret_cast<uint2*>(out + e) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
+  }
+}
+
 template <typename K>
 hipError_t allow_lds(K kernel, int bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
@@ -356,6 +549,7 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
     // dynamic LDS: FC1 staged rows + exponents; FC2 block table + slot tokens
     hipError_t e = allow_lds(&decode_fc1_kernel<FMT, true>, kDecodeStageBytes + 256);
     if (e == hipSuccess) e = allow_lds(&decode_fc2_kernel<FMT>, 98304);
+    if (e == hipSuccess) e = allow_lds(&decode_fc2_split_kernel<FMT, kF3RowGroups>, kF3MaxLds);
     return e;
   }();
   if (lds_ok != hipSuccess) return lds_ok;
@@ -369,11 +563,24 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
   else
     hipLaunchKernelGGL((decode_fc1_kernel<FMT, false>), dim3(grid1), dim3(kF1Threads), 0, stream, p);
   if (marks) (void)hipEventRecord(marks[0], stream);
-  const size_t lds2 = size_t(p.cap_blocks) * 4 + size_t(p.cap_blocks) * kBlockM * 4;
-  hipLaunchKernelGGL((decode_fc2_kernel<FMT>), dim3(g.n2_groups), dim3(kF2Threads), lds2, stream, p);
-  if (marks) {
-    (void)hipEventRecord(marks[1], stream);
-    (void)hipEventRecord(marks[2], stream);
+  constexpr int RG = kF3RowGroups;
+  const size_t lds3 = f3_lds_bytes<RG>(p.m, p.topk, p.cap_blocks);
+  // (the intermediate rows are addressed through a buffer resource: 32-bit offsets)
+  if (lds3 <= size_t(kF3MaxLds) && p.cap_blocks * kBlockM * g.ip * 2 <= int64_t(INT32_MAX)) {
+    const int nsplit = int((g.kb2 + kF3KB - 1) / kF3KB);
+    hipLaunchKernelGGL((decode_fc2_split_kernel<FMT, RG>), dim3((g.n2_groups + RG - 1) / RG, nsplit), dim3(kF3Threads), lds3, stream, p);
+    if (marks) (void)hipEventRecord(marks[1], stream);
+    const int64_t n4 = p.m * g.H / 4;
+    const int64_t cb = max(int64_t(1), min(int64_t(1024), (n4 + 255) / 256));
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(cb), dim3(256), 0, stream, p.part, p.out, p.m, int64_t(g.H), nsplit);
+    if (marks) (void)hipEventRecord(marks[2], stream);
+  } else {
+    const size_t lds2 = size_t(p.cap_blocks) * 4 + size_t(p.cap_blocks) * kBlockM * 4;
+    hipLaunchKernelGGL((decode_fc2_kernel<FMT>), dim3(g.n2_groups), dim3(kF2Threads), lds2, stream, p);
+    if (marks) {
+      (void)hipEventRecord(marks[1], stream);
+      (void)hipEventRecord(marks[2], stream);
+    }
   }
   return hipGetLastError();
 }

@@ -64,6 +64,7 @@ struct FusedParams {
   const uint16_t* x16;           // f16 [m, H] scaled activations (NVFP4 f16 MFMA route)
   const int32_t* xexp;           // [m] their per-token exponents
   float* y;                      // fp32 [m * topk, H] weighted FC2 rows per route (grouped GEMM)
+  float* part;                   // fp32 [K splits, m, H] FC2 partial sums (decode)
   int64_t cap_blocks;
   int64_t xs_pitch;              // decode FC1: elements per staged activation row in LDS
 };
