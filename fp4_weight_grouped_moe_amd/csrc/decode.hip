@@ -85,6 +85,9 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
   const int U2 = (U + 1) & ~1;                                // even: units are taken in pairs
   const int kb1 = int(g.kb1);
   const int sc_lane = FMT == FMT_NVFP4 ? ((lane >> 5) * 16 + col) * 16 : col * 16;
+  // FC2's per-group arrival counts start at zero in every call.
+  if (blockIdx.x == 0 && p.f2_count)
+    for (int i = tid; i < int(g.n2_groups); i += kF1Threads) p.f2_count[i] = 0;
   if (U == 0) return;
 
   // NVFP4 runs on the f16 MFMA: E2M1 x E4M3 weights are exact in f16, and the route-pack
@@ -347,14 +350,15 @@ __global__ __launch_bounds__(kF2Threads, 1) void decode_fc2_kernel(FusedParams p
 
 // ----------------------------------------------------------------------------- FC2, K split
 //
-// Workgroup (G, z) owns RG row groups (16 RG hidden rows) and K blocks 2z, 2z + 1 of the
+// Workgroup (z, G) owns RG row groups (16 RG hidden rows) and K blocks 2z, 2z + 1 of the
 // intermediate for every route block. That K slice of every valid route's intermediate row
 // is staged in LDS once (by DMA, row index = route id), so each LDS read of an MFMA B
 // fragment feeds RG MFMAs and the weight stream carries no other loads. Units are route
 // blocks (RG row groups x 2 K blocks = 2 RG KiB of nibbles), dealt to the 8 waves in turn;
 // a unit's route results are added into per-wave, per-token LDS sums. The workgroup's
-// fixed-order sum over waves is one fp32 partial per (K split, token, hidden row), and the
-// combine pass adds the K splits in order: deterministic, no global atomics.
+// fixed-order sum over waves is one fp32 partial per (K split, token, hidden row); the last
+// K split of a row group to finish (one arrival count per group) adds the partials in split
+// order and stores the bf16 rows: deterministic for any arrival order.
 
 constexpr int kF3Threads = 512;
 constexpr int kF3Waves = kF3Threads / 64;
@@ -362,6 +366,7 @@ constexpr int kF3KB = 2;             // K blocks per workgroup
 constexpr int kF3RowGroups = 2;      // row groups per workgroup
 constexpr int kF3MaxLds = 81920;     // two workgroups per CU
 constexpr int kF3RowBytes = kF3KB * kKBlock * 2;   // staged bytes per route row
+constexpr int kF3MaxRowDma = 8;      // 1 KiB row DMAs per wave: at most 64 KiB of staged rows
 
 template <int RG>
 struct F3Unit {
@@ -386,7 +391,16 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
   const int nb = p.live[2];
   const int m = int(p.m), topk = p.topk, routes = m * topk;
   const int kb2 = int(g.kb2), groups = int(g.n2_groups);
-  const int G = blockIdx.x, kq0 = int(blockIdx.y) * kF3KB;
+  // Workgroups come in pairs (K splits 2p, 2p + 1 of one row-group set) that run on the same
+  // XCD (workgroup i runs on XCD i % 8): the pair reads the two halves of the same 16-byte
+  // scale chunks and adjacent weight blocks, so the second read of each scale line is an L2
+  // hit. Pair L sits at workgroups 16 (L / 8) + L % 8 and 8 more.
+  const int nsplit = (kb2 + kF3KB - 1) / kF3KB, npair = (nsplit + 1) / 2;
+  const int ngroup = (groups + RG - 1) / RG;
+  const int pair = (int(blockIdx.x) >> 4) * 8 + (int(blockIdx.x) & 7);
+  const int z = 2 * (pair % npair) + ((int(blockIdx.x) >> 3) & 1), G = pair / npair;
+  if (G >= ngroup || z >= nsplit) return;
+  const int kq0 = z * kF3KB;
   uint8_t* bs = dyn;                                                        // [routes][kF3RowBytes]
   int* sroute = reinterpret_cast<int*>(dyn + f3_rows_bytes(routes));       // [nb * 16] slot -> route
   int* sexp = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(sroute) + f3_table_bytes(p.cap_blocks));    // [routes] f16 exponents
@@ -400,13 +414,20 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
   for (int i = tid; i < kF3Waves * m * 16 * RG; i += kF3Threads) tacc[i] = 0.f;
   const __amdgpu_buffer_rsrc_t tr = buffer_rsrc(p.sorted_route_ids, uint32_t(nb * kBlockM * 4));
   for (int n = wave; n * 64 < nb * kBlockM; n += kF3Waves) dma4(tr, sroute + 64 * n, uint32_t((64 * n + lane) * 4));
+  // The route -> slot lookups of all of a wave's rows go out together, then the row DMAs.
   const __amdgpu_buffer_rsrc_t ir = buffer_rsrc(p.inter, uint32_t(p.cap_blocks * kBlockM * g.ip * 2));
-  for (int n = wave; n * 1024 < routes * kF3RowBytes; n += kF3Waves) {
-    const int L = n * 1024 + lane * 16;
-    const int r = L / kF3RowBytes, o = L % kF3RowBytes;
-    const int slot = r < routes ? p.route_slot[r] : -1;
-    const bool ok = slot >= 0 && kq0 + o / (kKBlock * 2) < kb2;
-    dma16(ir, bs + n * 1024, ok ? uint32_t(slot * g.ip * 2 + kq0 * kKBlock * 2 + o) : kOutOfRange);
+  const int nchunk = int(f3_rows_bytes(routes) / 1024);
+  int slot[kF3MaxRowDma];
+#pragma unroll
+  for (int i = 0; i < kF3MaxRowDma; ++i) {
+    const int n = wave + kF3Waves * i, r = (n * 1024 + lane * 16) / kF3RowBytes;
+    slot[i] = n < nchunk && r < routes ? p.route_slot[r] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kF3MaxRowDma; ++i) {
+    const int n = wave + kF3Waves * i, o = (n * 1024 + lane * 16) % kF3RowBytes;
+    const bool ok = slot[i] >= 0 && kq0 + o / (kKBlock * 2) < kb2;
+    if (n < nchunk) dma16(ir, bs + n * 1024, ok ? uint32_t(slot[i] * g.ip * 2 + kq0 * kKBlock * 2 + o) : kOutOfRange);
   }
 
   // Loads are unconditional so that the wait counters stay exact: units past the end re-read
@@ -517,24 +538,44 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
     issue(u + 3, rb);
   }
   lds_barrier();
-  // Fixed-order sum over the waves: the partial of K split blockIdx.y for rows of this group.
+  // Fixed-order sum over the waves: the partial of K split z for rows of this group.
   for (int i = tid; i < m * 16 * RG; i += kF3Threads) {
     const int t = i / (16 * RG), row = i % (16 * RG);
     const int64_t h = int64_t(G) * 16 * RG + row;
     float sum = 0.f;
     for (int w = 0; w < kF3Waves; ++w) sum += tacc[(w * m + t) * (16 * RG) + row];
-    if (h < g.H) p.part[(int64_t(blockIdx.y) * m + t) * g.H + h] = sum;
+    if (h < g.H) __hip_atomic_store(p.part + (int64_t(z) * m + t) * g.H + h, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-}
-
-// out[t, h] = bf16 of the sum of the K-split partials in split order.
-__global__ void decode_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ out, int64_t m, int64_t H, int nsplit) {
-  const int64_t n4 = m * H / 4;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n4; i += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t e = i * 4;
-    f32x4 s = *reinterpret_cast<const f32x4*>(part + e);
-    for (int z = 1; z < nsplit; ++z) s += *reinterpret_cast<const f32x4*>(part + int64_t(z) * m * H + e);
-    *reinterpret_cast<uint2*>(out + e) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
+  // The last of the group's K splits to finish adds the partials in split order and stores
+  // the bf16 output rows. The partials are written and read as device-scope (relaxed
+  // atomic) accesses, which are coherent across the XCDs' L2s without flushing them; each
+  // thread waits for its stores to complete before the workgroup's count goes up. The
+  // counts were zeroed by the FC1 launch of the same call.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __shared__ int last;
+  if (tid == 0) last = __hip_atomic_fetch_add(p.f2_count + G, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+  __syncthreads();
+  if (!last) return;
+  for (int i = tid; i < m * 16 * RG; i += kF3Threads) {
+    const int t = i / (16 * RG), row = i % (16 * RG);
+    const int64_t h = int64_t(G) * 16 * RG + row;
+    if (h < g.H) {
+      // batches of 8 loads in flight, added in split order
+      float sum = 0.f;
+      for (int z0 = 0; z0 < nsplit; z0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          v[j] = z0 + j < nsplit ? __hip_atomic_load(p.part + (int64_t(z0 + j) * m + t) * g.H + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (z0 + j < nsplit) sum += v[j];
+      }
+      bf16x2 v;
+      v[0] = (__bf16)sum;
+      p.out[int64_t(t) * g.H + h] = __builtin_bit_cast(uint16_t, v[0]);
+    }
   }
 }
 
@@ -566,14 +607,15 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
   constexpr int RG = kF3RowGroups;
   const size_t lds3 = f3_lds_bytes<RG>(p.m, p.topk, p.cap_blocks);
   // (the intermediate rows are addressed through a buffer resource: 32-bit offsets)
-  if (lds3 <= size_t(kF3MaxLds) && p.cap_blocks * kBlockM * g.ip * 2 <= int64_t(INT32_MAX)) {
+  if (lds3 <= size_t(kF3MaxLds) && f3_rows_bytes(p.m * p.topk) <= size_t(kF3MaxRowDma) * kF3Waves * 1024 &&
+      p.cap_blocks * kBlockM * g.ip * 2 <= int64_t(INT32_MAX)) {
     const int nsplit = int((g.kb2 + kF3KB - 1) / kF3KB);
-    hipLaunchKernelGGL((decode_fc2_split_kernel<FMT, RG>), dim3((g.n2_groups + RG - 1) / RG, nsplit), dim3(kF3Threads), lds3, stream, p);
-    if (marks) (void)hipEventRecord(marks[1], stream);
-    const int64_t n4 = p.m * g.H / 4;
-    const int64_t cb = max(int64_t(1), min(int64_t(1024), (n4 + 255) / 256));
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(cb), dim3(256), 0, stream, p.part, p.out, p.m, int64_t(g.H), nsplit);
-    if (marks) (void)hipEventRecord(marks[2], stream);
+    const int64_t pairs = ((g.n2_groups + RG - 1) / RG) * ((nsplit + 1) / 2);
+    hipLaunchKernelGGL((decode_fc2_split_kernel<FMT, RG>), dim3((pairs + 7) / 8 * 16), dim3(kF3Threads), lds3, stream, p);
+    if (marks) {
+      (void)hipEventRecord(marks[1], stream);
+      (void)hipEventRecord(marks[2], stream);
+    }
   } else {
     const size_t lds2 = size_t(p.cap_blocks) * 4 + size_t(p.cap_blocks) * kBlockM * 4;
     hipLaunchKernelGGL((decode_fc2_kernel<FMT>), dim3(g.n2_groups), dim3(kF2Threads), lds2, stream, p);

@@ -65,6 +65,7 @@ struct FusedParams {
   const int32_t* xexp;           // [m] their per-token exponents
   float* y;                      // fp32 [m * topk, H] weighted FC2 rows per route (grouped GEMM)
   float* part;                   // fp32 [K splits, m, H] FC2 partial sums (decode)
+  int32_t* f2_count;             // [n2_groups] FC2 K-split arrival counts (decode)
   int64_t cap_blocks;
   int64_t xs_pitch;              // decode FC1: elements per staged activation row in LDS
 };

@@ -108,10 +108,10 @@ inline bool decode_stages_x(const PreparedGeom& g, int64_t m) { return m * decod
 // Fused-layer workspace: route pack (block 16), bf16 intermediate rows per packed slot, the
 // f16 copy of the activations with per-token exponents (NVFP4), for the grouped-GEMM path
 // the fp32 FC2 row of every route, summed over top-k by the combine pass, and for the
-// decode path the fp32 FC2 partial sums of each K split.
+// decode path the fp32 FC2 partial sums of each K split with their arrival counts.
 struct FusedGeom {
   PackGeom pack;
-  size_t off_pack, off_inter, off_x16, off_xexp, off_y, off_part, total;
+  size_t off_pack, off_inter, off_x16, off_xexp, off_y, off_part, off_count, total;
 };
 
 __host__ __device__ inline FusedGeom make_fused_geom(const PreparedGeom& w, int64_t cap, int64_t k) {
@@ -125,6 +125,7 @@ __host__ __device__ inline FusedGeom make_fused_geom(const PreparedGeom& w, int6
   f.off_y = o;     o = align256(o + size_t(cap) * k * w.H * 4);
   // decode FC2 partial sums: one fp32 [cap, H] slab per pair of intermediate K blocks
   f.off_part = o;  o = align256(o + (cap <= kDecodeMaxM ? size_t((w.kb2 + 1) / 2) * cap * w.H * 4 : 0));
+  f.off_count = o; o = align256(o + (cap <= kDecodeMaxM ? size_t(w.n2_groups) * 4 : 0));
   f.total = o;
   return f;
 }
