@@ -70,7 +70,7 @@ struct FusedParams {
   int64_t xs_pitch;              // decode FC1: elements per staged activation row in LDS
 };
 
-size_t route_pack_lds_bytes(int num_experts);
+size_t route_pack_lds_bytes(int num_experts, int64_t num_routes);
 // `side_blocks` extra workgroups do the activation conversion when p.x16 is set.
 hipError_t launch_route_pack(const RoutePackParams& p, int side_blocks, hipStream_t stream);
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);

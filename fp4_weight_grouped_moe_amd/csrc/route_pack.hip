@@ -18,6 +18,10 @@ namespace {
 constexpr int kPackThreads = 1024;
 constexpr int kPackWaves = kPackThreads / 64;
 constexpr int kValidSlot = 36;                 // scan scratch entries 0 .. 2 kPackWaves + 1 are the scans'
+__host__ __device__ inline size_t route_pack_base_lds(int num_experts) {
+  // counts, scan scratch, kept counts, per-wave counts; rounded to 16 bytes
+  return (size_t(num_experts) * 8 + 40 * 4 + size_t(kPackWaves) * num_experts + 16 + 15) / 16 * 16;
+}
 constexpr int kRowRegs = 8;                    // 16-byte chunks per lane per batch of the row conversion
 
 __device__ __forceinline__ int local_expert(const RoutePackParams& p, int64_t r) {
@@ -26,6 +30,42 @@ __device__ __forceinline__ int local_expert(const RoutePackParams& p, int64_t r)
   if (g < 0 || g >= p.num_global_experts) return -1;
   int l = p.expert_map ? p.expert_map[g] : g;
   return (l >= 0 && l < p.num_experts) ? l : -1;
+}
+
+// Batches of more than one chunk and at most kCacheRoutes routes keep every route's local id
+// (int16) and router weight in LDS: they are read from memory once, in batches of kLoadBatch loads per thread, and the
+// count and scatter passes work from LDS.
+constexpr int kCacheRoutes = 16384;
+constexpr int kLoadBatch = 8;
+
+__device__ void cache_routes(const RoutePackParams& p, int16_t* lc, float* wc, int* cnt) {
+  const int tid = threadIdx.x;
+  const int64_t R = p.num_routes;
+  for (int64_t base = 0; base < R; base += int64_t(kPackThreads) * kLoadBatch) {
+    int g[kLoadBatch];
+    float w[kLoadBatch];
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j) {
+      const int64_t r = base + j * kPackThreads + tid;
+      g[j] = r < R ? p.topk_ids[r] : -1;
+      w[j] = (r < R && p.topk_weights) ? p.topk_weights[r] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j) {
+      const bool ok = g[j] >= 0 && g[j] < p.num_global_experts;
+      g[j] = ok ? (p.expert_map ? p.expert_map[g[j]] : g[j]) : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j) {
+      const int64_t r = base + j * kPackThreads + tid;
+      const int l = (g[j] >= 0 && g[j] < p.num_experts) ? g[j] : -1;
+      if (r < R) {
+        lc[r] = int16_t(l);
+        wc[r] = w[j];
+        if (l >= 0) atomicAdd(&cnt[l], 1);
+      }
+    }
+  }
 }
 
 // Exclusive scan of one int per thread over the 1024-thread workgroup.
@@ -96,19 +136,27 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   int* wave_tot = cnt + E;                                 // [40] scan scratch; [kValidSlot] = valid routes
   int* ecnt = wave_tot + 40;                               // [E] counts (kept for the tile table)
   uint8_t* wcnt = reinterpret_cast<uint8_t*>(ecnt + E);    // [kPackWaves][E] per-wave counts
+  const bool cached = p.num_routes > kPackThreads && p.num_routes <= kCacheRoutes;
+  int16_t* lc = reinterpret_cast<int16_t*>(smem + route_pack_base_lds(E));      // [R] local ids
+  float* wc = reinterpret_cast<float*>(smem + route_pack_base_lds(E) + size_t(kCacheRoutes) * 2);   // [R] weights
 
-  // The first chunk's local id and router weight stay in registers for the scatter, so
-  // small batches read topk_ids / expert_map / topk_weights from memory only once.
-  const int l_first = local_expert(p, tid);
-  const float w_first = (p.topk_weights && tid < p.num_routes) ? p.topk_weights[tid] : 0.f;
+  // Small batches (one chunk) keep the first chunk's local id and router weight in
+  // registers; larger ones up to kCacheRoutes keep every route's in LDS. Either way
+  // topk_ids / expert_map / topk_weights are read from memory once.
+  const int l_first = cached ? -1 : local_expert(p, tid);
+  const float w_first = (!cached && p.topk_weights && tid < p.num_routes) ? p.topk_weights[tid] : 0.f;
   for (int e = tid; e < E; e += kPackThreads) cnt[e] = 0;
   if (tid == 0) wave_tot[kValidSlot] = 0;
   for (int i = tid; i < kPackWaves * E; i += kPackThreads) wcnt[i] = 0;
   __syncthreads();
-  if (l_first >= 0) atomicAdd(&cnt[l_first], 1);
-  for (int64_t r = kPackThreads + tid; r < p.num_routes; r += kPackThreads) {
-    int l = local_expert(p, r);
-    if (l >= 0) atomicAdd(&cnt[l], 1);
+  if (cached) {
+    cache_routes(p, lc, wc, cnt);
+  } else {
+    if (l_first >= 0) atomicAdd(&cnt[l_first], 1);
+    for (int64_t r = kPackThreads + tid; r < p.num_routes; r += kPackThreads) {
+      int l = local_expert(p, r);
+      if (l >= 0) atomicAdd(&cnt[l], 1);
+    }
   }
   __syncthreads();
 
@@ -182,7 +230,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   int valid_total = 0;
   for (int64_t base = 0; base < p.num_routes; base += kPackThreads) {
     const int64_t r = base + tid;
-    const int l = base == 0 ? l_first : local_expert(p, r);
+    const int l = cached ? (r < p.num_routes ? int(lc[r]) : -1) : base == 0 ? l_first : local_expert(p, r);
     // Stable rank among the wave's earlier lanes with the same expert, and the wave's count
     // per expert (written by the expert's first lane): one pass over the 64 lanes' ids.
     int rank = 0, same = 0;
@@ -205,7 +253,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
       p.sorted_route_ids[pos] = int(r);
       p.route_slot[r] = pos;
       if (p.slot_info) {
-        const float wt = base == 0 ? w_first : (p.topk_weights ? p.topk_weights[r] : 0.f);
+        const float wt = cached ? wc[r] : base == 0 ? w_first : (p.topk_weights ? p.topk_weights[r] : 0.f);
         p.slot_info[pos] = make_int2(int(r / p.topk), __float_as_int(wt));
       }
     } else if (r < p.num_routes) {
@@ -308,12 +356,17 @@ __global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParam
   }
 }
 
-size_t route_pack_lds_bytes(int num_experts) {
-  return size_t(num_experts) * 8 + 40 * 4 + size_t(kPackWaves) * num_experts + 16;
+size_t route_pack_lds_bytes(int num_experts, int64_t num_routes) {
+  const bool cached = num_routes > kPackThreads && num_routes <= kCacheRoutes;
+  return route_pack_base_lds(num_experts) + (cached ? size_t(kCacheRoutes) * 6 : 0);
 }
 
 hipError_t launch_route_pack(const RoutePackParams& p, int side_blocks, hipStream_t stream) {
-  const size_t lds = route_pack_lds_bytes(p.num_experts);
+  static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_pack_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       int(route_pack_base_lds(kMaxExperts) + size_t(kCacheRoutes) * 6));
+  if (lds_ok != hipSuccess) return lds_ok;
+  const size_t lds = route_pack_lds_bytes(p.num_experts, p.num_routes);
   hipLaunchKernelGGL(route_pack_kernel, dim3(1 + (p.x16 ? side_blocks : 0)), dim3(kPackThreads), lds, stream, p);
   return hipGetLastError();
 }
