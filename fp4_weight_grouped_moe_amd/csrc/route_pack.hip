@@ -32,23 +32,29 @@ __device__ __forceinline__ int local_expert(const RoutePackParams& p, int64_t r)
   return (l >= 0 && l < p.num_experts) ? l : -1;
 }
 
-// Batches of more than one chunk and at most kCacheRoutes routes keep every route's local id
-// (int16) and router weight in LDS: they are read from memory once, in batches of kLoadBatch loads per thread, and the
-// count and scatter passes work from LDS.
+// Batches of more than one chunk and at most kCacheRoutes routes over at most kSegExperts
+// experts keep every route's local id (int16) in LDS, read once in batches of kLoadBatch
+// loads per thread, and scatter by wave segments: wave w ranks its contiguous segment of
+// routes 64 at a time against its own running per-expert counts (no barriers), one scan over
+// the waves turns the counts into segment bases, and every route's slot is its segment base
+// plus its rank. Two barriers in all, instead of three per 1024 routes.
 constexpr int kCacheRoutes = 16384;
+constexpr int kSegExperts = 1024;
 constexpr int kLoadBatch = 8;
 
-__device__ void cache_routes(const RoutePackParams& p, int16_t* lc, float* wc, int* cnt) {
+__host__ __device__ inline bool segmented_pack(int64_t num_routes, int num_experts) {
+  return num_routes > kPackThreads && num_routes <= kCacheRoutes && num_experts <= kSegExperts;
+}
+
+__device__ void cache_routes(const RoutePackParams& p, int16_t* lc, int* cnt) {
   const int tid = threadIdx.x;
   const int64_t R = p.num_routes;
   for (int64_t base = 0; base < R; base += int64_t(kPackThreads) * kLoadBatch) {
     int g[kLoadBatch];
-    float w[kLoadBatch];
 #pragma unroll
     for (int j = 0; j < kLoadBatch; ++j) {
       const int64_t r = base + j * kPackThreads + tid;
       g[j] = r < R ? p.topk_ids[r] : -1;
-      w[j] = (r < R && p.topk_weights) ? p.topk_weights[r] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < kLoadBatch; ++j) {
@@ -61,7 +67,6 @@ __device__ void cache_routes(const RoutePackParams& p, int16_t* lc, float* wc, i
       const int l = (g[j] >= 0 && g[j] < p.num_experts) ? g[j] : -1;
       if (r < R) {
         lc[r] = int16_t(l);
-        wc[r] = w[j];
         if (l >= 0) atomicAdd(&cnt[l], 1);
       }
     }
@@ -136,9 +141,10 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   int* wave_tot = cnt + E;                                 // [40] scan scratch; [kValidSlot] = valid routes
   int* ecnt = wave_tot + 40;                               // [E] counts (kept for the tile table)
   uint8_t* wcnt = reinterpret_cast<uint8_t*>(ecnt + E);    // [kPackWaves][E] per-wave counts
-  const bool cached = p.num_routes > kPackThreads && p.num_routes <= kCacheRoutes;
-  int16_t* lc = reinterpret_cast<int16_t*>(smem + route_pack_base_lds(E));      // [R] local ids
-  float* wc = reinterpret_cast<float*>(smem + route_pack_base_lds(E) + size_t(kCacheRoutes) * 2);   // [R] weights
+  const bool cached = segmented_pack(p.num_routes, E);
+  int16_t* lc = reinterpret_cast<int16_t*>(smem + route_pack_base_lds(E));                          // [R] local ids
+  uint16_t* srank = reinterpret_cast<uint16_t*>(smem + route_pack_base_lds(E) + size_t(kCacheRoutes) * 2);   // [R] rank in segment
+  uint16_t* scnt = srank + kCacheRoutes;                                                            // [waves][E] counts, then bases
 
   // Small batches (one chunk) keep the first chunk's local id and router weight in
   // registers; larger ones up to kCacheRoutes keep every route's in LDS. Either way
@@ -148,9 +154,11 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   for (int e = tid; e < E; e += kPackThreads) cnt[e] = 0;
   if (tid == 0) wave_tot[kValidSlot] = 0;
   for (int i = tid; i < kPackWaves * E; i += kPackThreads) wcnt[i] = 0;
+  if (cached)
+    for (int i = tid; i < kPackWaves * E; i += kPackThreads) scnt[i] = 0;
   __syncthreads();
   if (cached) {
-    cache_routes(p, lc, wc, cnt);
+    cache_routes(p, lc, cnt);
   } else {
     if (l_first >= 0) atomicAdd(&cnt[l_first], 1);
     for (int64_t r = kPackThreads + tid; r < p.num_routes; r += kPackThreads) {
@@ -225,12 +233,66 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   for (int64_t r = p.num_routes + tid; r < p.cap_k; r += kPackThreads) p.route_slot[r] = -1;
   __syncthreads();
 
+  int valid_total = 0;
+  if (cached) {
+    // Wave segments (see cache_routes): ranks against the wave's running counts.
+    const int R = int(p.num_routes);
+    const int S = ((R + kPackWaves - 1) / kPackWaves + 63) / 64 * 64;
+    const int s0 = wave * S, s1 = min(R, s0 + S);
+    uint16_t* myc = scnt + wave * E;
+    const uint64_t lt_mask = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    for (int j0 = s0; j0 < s1; j0 += 64) {
+      const int r = j0 + lane;
+      const int l = r < s1 ? int(lc[r]) : -1;
+      // One pass per distinct expert among the 64 routes: the lanes of expert v are one
+      // ballot; a lane's rank is the number of them below it.
+      int rank = 0, same = 0;
+      uint64_t todo = __ballot(l >= 0);
+      valid_total += __popcll(todo);
+      while (todo) {
+        const int v = __builtin_amdgcn_readlane(l, __builtin_ctzll(todo));
+        const uint64_t mv = __ballot(l == v);
+        if (l == v) {
+          rank = __popcll(mv & lt_mask);
+          same = __popcll(mv);
+        }
+        todo &= ~mv;
+      }
+      // Every lane reads the running count before the expert's first lane bumps it (one
+      // wave's LDS operations complete in order).
+      const int run = l >= 0 ? int(myc[l]) : 0;
+      if (r < s1) srank[r] = uint16_t(run + rank);
+      if (l >= 0 && rank == 0) myc[l] = uint16_t(run + same);
+    }
+    __syncthreads();
+    // Segment bases: expert e's slots for wave w start after the earlier waves' routes of e.
+    for (int e = tid; e < E; e += kPackThreads) {
+      int run = cnt[e];
+      for (int w2 = 0; w2 < kPackWaves; ++w2) {
+        const int c = scnt[w2 * E + e];
+        scnt[w2 * E + e] = uint16_t(run);
+        run += c;
+      }
+    }
+    __syncthreads();
+    for (int r = tid; r < R; r += kPackThreads) {
+      const int l = lc[r];
+      if (l >= 0) {
+        const int pos = int(scnt[(r / S) * E + l]) + int(srank[r]);
+        p.sorted_route_ids[pos] = r;
+        p.route_slot[r] = pos;
+        if (p.slot_info)
+          p.slot_info[pos] = make_int2(r / p.topk, __float_as_int(p.topk_weights ? p.topk_weights[r] : 0.f));
+      } else {
+        p.route_slot[r] = -1;
+      }
+    }
+  }
   // Stable scatter, 1024 routes per chunk: rank inside the wave by matching equal expert
   // ids, then add the counts of lower waves of the chunk and the running slot.
-  int valid_total = 0;
-  for (int64_t base = 0; base < p.num_routes; base += kPackThreads) {
+  for (int64_t base = 0; base < (cached ? 0 : p.num_routes); base += kPackThreads) {
     const int64_t r = base + tid;
-    const int l = cached ? (r < p.num_routes ? int(lc[r]) : -1) : base == 0 ? l_first : local_expert(p, r);
+    const int l = base == 0 ? l_first : local_expert(p, r);
     // Stable rank among the wave's earlier lanes with the same expert, and the wave's count
     // per expert (written by the expert's first lane): one pass over the 64 lanes' ids.
     int rank = 0, same = 0;
@@ -253,7 +315,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
       p.sorted_route_ids[pos] = int(r);
       p.route_slot[r] = pos;
       if (p.slot_info) {
-        const float wt = cached ? wc[r] : base == 0 ? w_first : (p.topk_weights ? p.topk_weights[r] : 0.f);
+        const float wt = base == 0 ? w_first : (p.topk_weights ? p.topk_weights[r] : 0.f);
         p.slot_info[pos] = make_int2(int(r / p.topk), __float_as_int(wt));
       }
     } else if (r < p.num_routes) {
@@ -357,14 +419,14 @@ __global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParam
 }
 
 size_t route_pack_lds_bytes(int num_experts, int64_t num_routes) {
-  const bool cached = num_routes > kPackThreads && num_routes <= kCacheRoutes;
-  return route_pack_base_lds(num_experts) + (cached ? size_t(kCacheRoutes) * 6 : 0);
+  return route_pack_base_lds(num_experts) +
+         (segmented_pack(num_routes, num_experts) ? size_t(kCacheRoutes) * 4 + size_t(kPackWaves) * num_experts * 2 : 0);
 }
 
 hipError_t launch_route_pack(const RoutePackParams& p, int side_blocks, hipStream_t stream) {
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_pack_kernel),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       int(route_pack_base_lds(kMaxExperts) + size_t(kCacheRoutes) * 6));
+                                                       int(route_pack_lds_bytes(kSegExperts, kCacheRoutes)));
   if (lds_ok != hipSuccess) return lds_ok;
   const size_t lds = route_pack_lds_bytes(p.num_experts, p.num_routes);
   hipLaunchKernelGGL(route_pack_kernel, dim3(1 + (p.x16 ? side_blocks : 0)), dim3(kPackThreads), lds, stream, p);
