@@ -228,7 +228,7 @@ def main():
     step_bytes = weight_bytes + 2 * m * H * 2
     flops = avg_valid * 2.0 * (H * cfg.n1 + cfg.inter * H)
     t = ms_per_step * 1e-3
-    decode_path = args.path == "decode" or (args.path == "auto" and m <= 8)
+    decode_path = args.path == "decode" or (args.path == "auto" and m <= moe.MOE_DECODE_MAX_M and cap <= moe.MOE_DECODE_MAX_M)
     kernel_src = "decode.hip" if decode_path else "gemm.hip"
     if decode_path:
         # dominant kernel: FC1 (W13 is two thirds of the streamed weights)

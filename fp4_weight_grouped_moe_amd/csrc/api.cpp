@@ -48,9 +48,9 @@ int initial_path() {
 
 int initial_decode_max_m() {
   const char* s = std::getenv("MOE_W4A16_DECODE_MAX_M");
-  if (!s) return 8;
+  if (!s) return MOE_DECODE_MAX_M;
   int v = std::atoi(s);
-  return (v >= 0 && v <= MOE_DECODE_MAX_M) ? v : 8;
+  return (v >= 0 && v <= MOE_DECODE_MAX_M) ? v : MOE_DECODE_MAX_M;
 }
 
 std::mutex g_cfg_mu;

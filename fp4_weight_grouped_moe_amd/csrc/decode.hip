@@ -598,7 +598,8 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
   const PreparedGeom& g = p.g;
   p.xs_pitch = decode_x_pitch(g);
   const int64_t items = p.cap_blocks * (g.n1_groups / 2);
-  const int64_t grid1 = max(int64_t(1), min(items, int64_t(num_cus) * 2));
+  const bool two_per_cu = p.m * p.xs_pitch * 2 <= kDecodeStageTwoPerCU;   // else the LDS holds one workgroup
+  const int64_t grid1 = max(int64_t(1), min(items, int64_t(num_cus) * (two_per_cu ? 2 : 1)));
   if (decode_stages_x(g, p.m))
     hipLaunchKernelGGL((decode_fc1_kernel<FMT, true>), dim3(grid1), dim3(kF1Threads), size_t(p.m) * p.xs_pitch * 2 + 256, stream, p);
   else

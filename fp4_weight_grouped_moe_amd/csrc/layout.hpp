@@ -97,11 +97,13 @@ __host__ __device__ inline PackGeom make_pack_geom(int64_t cap, int64_t k, int64
 }
 
 constexpr int kDecodeMaxM = 16;          // token columns of the decode path
-constexpr int kDecodeStageBytes = 65536; // LDS for the decode kernels' staged activation rows
+constexpr int kDecodeStageBytes = 147456; // LDS for the decode FC1 staged activation rows (144 KiB)
+constexpr int kDecodeStageTwoPerCU = 65536;  // at most this much keeps two FC1 workgroups per CU
 
 // Decode FC1 keeps the activation rows in LDS when they fit, at a pitch of hp rounded up to
-// 512 elements (whole 1 KiB rows of LDS DMA). With NVFP4 weights the staged rows are the f16
-// copy made by the route-pack launch.
+// 512 elements (whole 1 KiB rows of LDS DMA); up to 64 KiB of rows two workgroups share a
+// CU, beyond that one. With NVFP4 weights the staged rows are the f16 copy made by the
+// route-pack launch.
 inline int64_t decode_x_pitch(const PreparedGeom& g) { return (g.hp + 511) / 512 * 512; }
 inline bool decode_stages_x(const PreparedGeom& g, int64_t m) { return m * decode_x_pitch(g) * 2 <= kDecodeStageBytes; }
 

@@ -143,8 +143,9 @@ int moe_w4a16_prepare(const moe_w4a16_dims* dims, const uint8_t* w13, const uint
  *
  * A call whose m is at most the decode threshold and whose token_capacity is at most
  * MOE_DECODE_MAX_M takes the decode path: two weight-streaming MFMA kernels; FC2 gives
- * each workgroup a range of hidden rows for every route and sums each token's routes in
- * LDS before one bf16 store. Other calls take the grouped-GEMM path: FC1 + activation
+ * each workgroup a range of hidden rows and a slice of K for every route, sums each
+ * token's routes in LDS, and the last K slice of a row range to finish adds the slices in
+ * order before one bf16 store. Other calls take the grouped-GEMM path: FC1 + activation
  * epilogue over (route tile, weight tile) items, FC2 writing each route's weighted fp32
  * row, and a combine pass that sums every token's top-k rows in route order and casts to
  * bf16 -- deterministic, no atomics on data. Persistent workgroups take items from a
@@ -188,7 +189,8 @@ const char* moe_last_error(void);
  * initial value. Returns the previous value, or MOE_ERR_INVALID_ARG. */
 int moe_w4a16_set_path(int path);
 
-/* Decode threshold (default 8; MOE_W4A16_DECODE_MAX_M overrides it at load).
+/* Decode threshold (default MOE_DECODE_MAX_M, measured faster than the grouped GEMM at
+ * every m up to it; MOE_W4A16_DECODE_MAX_M overrides it at load).
  * Values outside [0, MOE_DECODE_MAX_M] are rejected. Returns the previous value. */
 int moe_w4a16_set_decode_max_m(int max_m);
 

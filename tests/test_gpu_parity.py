@@ -329,6 +329,29 @@ def _full_case(name, m, device, codes_dev=None):
     return case
 
 
+@pytest.mark.parametrize("name,m", [("decode", 12), ("decode", 16), ("small", 16)])
+def test_decode_path_full_size_above_eight_tokens(moe, device, name, m):
+    """The decode path at 9..16 tokens stages more than 64 KiB of activation rows (one FC1
+    workgroup per CU): sampled full-size outputs against the oracle."""
+    cfg = C.get_config(name)
+    case = _full_case(name, m, device)
+    layer = make_layer(case, device, token_capacity=RP.token_capacity(m))
+    _say(f"full {name} m={m} path=decode")
+    moe.moe_w4a16_set_path("decode")
+    try:
+        out = run_layer(layer, case, device)
+    finally:
+        moe.moe_w4a16_set_path("auto")
+    got = bf16_tensor_to_f64(out)
+    rng = np.random.default_rng(11)
+    tokens = np.unique(np.array([0, m - 1, rng.integers(0, m)]))
+    cols = np.sort(rng.choice(cfg.hidden, size=96, replace=False))
+    _check(case, got, tokens=tokens, cols=cols, label=f"{name} m={m} decode")
+    assert np.all(np.isfinite(got))
+    del layer, case
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name,ms", [("decode", (1, 4, 8)), ("small", (16, 64)), ("prefill", (2048,)),
                                      ("edge", (512, 300, 511))])
 def test_fused_full_size_sampled(moe, device, name, ms):
