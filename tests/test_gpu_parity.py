@@ -246,6 +246,28 @@ def test_gemm_repeat_runs_over_a_dirty_workspace(moe, device, name, m):
         moe.moe_w4a16_set_path("auto")
 
 
+@pytest.mark.parametrize("name,m", [("decode_s", 8), ("decode_s", 16), ("small_s", 16)])
+def test_decode_repeat_runs_over_a_dirty_workspace(moe, device, name, m):
+    """The decode path reads nothing it did not write in the same call: the FC2 K-split arrival
+    counts are zeroed by FC1 and every partial is written before its count goes up, so runs over
+    a workspace holding garbage, and back-to-back runs with no refill, all match the oracle."""
+    cfg = SCALED[name]
+    _say(f"decode repeat {name} m={m}")
+    case = make_case(cfg, m, seed=cfg.index * 7 + m, weights="normal")
+    layer = make_layer(case, device)
+    ref = oracle_out(case)
+    moe.moe_w4a16_set_path("decode")
+    try:
+        for rep in range(6):
+            if rep % 2 == 0:
+                layer.workspace.fill_(0x7F if rep % 4 == 0 else 0xFF)
+            got = bf16_tensor_to_f64(run_layer(layer, case, device))
+            ok, err, bound = M.within_tolerance(got, ref)
+            assert ok, f"{name} m={m} run {rep}: {err} > {bound}"
+    finally:
+        moe.moe_w4a16_set_path("auto")
+
+
 def test_fused_capacity_reuse_one_workspace(moe, device):
     cfg = SCALED["edge_s"]
     case0 = make_case(cfg, 128, seed=41, weights="normal")
