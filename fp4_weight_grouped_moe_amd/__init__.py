@@ -79,6 +79,7 @@ def _load():
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_w4a16_set_path": (I32, [I32]),
         "moe_w4a16_set_decode_max_m": (I32, [I32]),
+        "moe_router_topk": (I32, [P, I64, I32, I32, I32, I32, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -90,7 +91,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("moe_route_pack_token_capacity", "moe_route_pack_workspace_size", "moe_route_pack",
             "moe_w4a16_prepared_size", "moe_w4a16_prepare", "moe_w4a16_workspace_size", "moe_w4a16_fused",
-            "moe_w4a16_fused_profiled", "moe_last_error", "moe_w4a16_set_path", "moe_w4a16_set_decode_max_m")
+            "moe_w4a16_fused_profiled", "moe_last_error", "moe_w4a16_set_path", "moe_w4a16_set_decode_max_m",
+            "moe_router_topk")
 
 
 def lib():
@@ -187,6 +189,17 @@ def moe_w4a16_fused_profiled(dims: moe_w4a16_dims, prepared, prepared_bytes: int
                                          _ptr(topk_ids), _ptr(topk_weights), topk, _ptr(expert_map),
                                          num_global_experts, token_capacity, _ptr(workspace), workspace_bytes,
                                          _ptr(out), _stream(stream), arr, len(events)), "moe_w4a16_fused_profiled")
+
+
+ROUTER_SCORING = {"softmax": 0, "sigmoid": 1}
+
+
+def moe_router_topk(logits, m: int, num_experts: int, topk: int, scoring, renormalize: bool, topk_ids,
+                    topk_weights, stream=None) -> None:
+    """Top-k experts and weights of fp32 logits [m, num_experts] (device tensors)."""
+    _check(_lib.moe_router_topk(_ptr(logits), m, num_experts, topk, ROUTER_SCORING.get(scoring, scoring),
+                                1 if renormalize else 0, _ptr(topk_ids), _ptr(topk_weights), _stream(stream)),
+           "moe_router_topk")
 
 
 def moe_w4a16_set_path(path) -> int:

@@ -374,6 +374,30 @@ int moe_w4a16_set_path(int path) {
   return prev;
 }
 
+int moe_router_topk(const float* logits, int64_t m, int num_experts, int topk, int scoring, int renormalize,
+                    int32_t* topk_ids, float* topk_weights, hipStream_t stream) {
+  if (m < 0) return fail(MOE_ERR_INVALID_ARG, "m = %lld is negative", (long long)m);
+  if (num_experts < 1 || num_experts > kRouterMaxExperts)
+    return fail(MOE_ERR_INVALID_ARG, "num_experts %d outside [1, %d]", num_experts, kRouterMaxExperts);
+  if (topk < 1 || topk > kRouterMaxTopk || topk > num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "topk %d outside [1, min(%d, num_experts = %d)]", topk, kRouterMaxTopk, num_experts);
+  if (scoring != MOE_ROUTER_SOFTMAX && scoring != MOE_ROUTER_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARG, "unknown scoring %d", scoring);
+  if (m > 0 && (!logits || !topk_ids || !topk_weights)) return fail(MOE_ERR_INVALID_ARG, "NULL device pointer");
+  int cus = 0;
+  if (int rc = check_device(&cus); rc != MOE_OK) return rc;
+  RouterParams p{};
+  p.logits = logits;
+  p.m = m;
+  p.num_experts = num_experts;
+  p.topk = topk;
+  p.scoring = scoring;
+  p.renormalize = renormalize ? 1 : 0;
+  p.topk_ids = topk_ids;
+  p.topk_weights = topk_weights;
+  return launch_status(launch_router(p, stream), "router launch");
+}
+
 int moe_w4a16_set_decode_max_m(int max_m) {
   if (max_m < 0 || max_m > MOE_DECODE_MAX_M) return fail(MOE_ERR_INVALID_ARG, "decode max m %d outside [0, %d]", max_m, MOE_DECODE_MAX_M);
   std::lock_guard<std::mutex> lk(g_cfg_mu);

@@ -70,6 +70,20 @@ struct FusedParams {
   int64_t xs_pitch;              // decode FC1: elements per staged activation row in LDS
 };
 
+// Router front end: top-k of fp32 logits [m, num_experts] per token.
+struct RouterParams {
+  const float* logits;
+  int64_t m;
+  int32_t num_experts, topk;
+  int32_t scoring;               // 0 softmax, 1 sigmoid
+  int32_t renormalize;
+  int32_t* topk_ids;
+  float* topk_weights;
+};
+constexpr int kRouterMaxExperts = 1024;
+constexpr int kRouterMaxTopk = 64;
+hipError_t launch_router(const RouterParams& p, hipStream_t stream);
+
 size_t route_pack_lds_bytes(int num_experts, int64_t num_routes);
 // `side_blocks` extra workgroups do the activation conversion when p.x16 is set.
 hipError_t launch_route_pack(const RoutePackParams& p, int side_blocks, hipStream_t stream);

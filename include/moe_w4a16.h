@@ -179,6 +179,30 @@ int moe_w4a16_fused_profiled(const moe_w4a16_dims* dims, const void* prepared, s
                              size_t workspace_bytes, uint16_t* out, hipStream_t stream,
                              hipEvent_t* events, int num_events);
 
+/* ------------------------------------------------------------------ router front end
+ * Page: Summary (New Features: configurable routing) and Walkthrough (kernel compilation and
+ * execution: routing modes); the pages print no formula, so the operation follows the
+ * workload definitions (softmax top-k over the router logits; sigmoid scores, top-k,
+ * renormalised):
+ *   topk_ids[t, j]     = the j-th largest of logits[t, :] (equal logits: ascending expert id;
+ *                        the comparison is on the fp32 values, -0 equal to +0),
+ *   topk_weights[t, j] = score of that expert, score = softmax or sigmoid of the logits,
+ *                        divided by the sum of the k selected scores when renormalize != 0
+ *                        (for softmax this is the softmax of the k selected logits).
+ * logits: device fp32 [m, num_experts], finite values, row-major. topk_ids: device int32
+ * [m, topk]; topk_weights: device fp32 [m, topk]; both caller-owned, written in selection
+ * order. One wave per token; no allocation, no synchronisation.
+ * Errors: MOE_ERR_INVALID_ARG for m < 0, num_experts outside [1, 1024], topk outside
+ * [1, min(64, num_experts)], an unknown scoring, or NULL pointers with m > 0;
+ * MOE_ERR_UNSUPPORTED off gfx950; MOE_ERR_HIP when the launch fails. */
+typedef enum moe_router_scoring {
+  MOE_ROUTER_SOFTMAX = 0,
+  MOE_ROUTER_SIGMOID = 1
+} moe_router_scoring;
+
+int moe_router_topk(const float* logits, int64_t m, int num_experts, int topk, int scoring, int renormalize,
+                    int32_t* topk_ids, float* topk_weights, hipStream_t stream);
+
 /* Message for the calling thread's last failing call ("" if none). */
 const char* moe_last_error(void);
 

@@ -70,6 +70,17 @@ def draw_routing(cfg: Workload, m: int, seed: int):
     return ids, w, emap, rng
 
 
+def draw_router_logits(cfg: Workload, m: int, seed: int) -> np.ndarray:
+    """Router logits fp32 [m, Eg] for the router front end: N(0,1), plus the Zipf recipe's
+    -s*ln(e+1) for expert e when the workload uses it (the same draw as draw_routing's)."""
+    rng = _rng(seed)
+    eg = cfg.num_global_experts
+    logits = rng.standard_normal((m, eg))
+    if cfg.routing == "zipf":
+        logits = logits - cfg.zipf_s * np.log(np.arange(eg, dtype=np.float64) + 1.0)[None, :]
+    return logits.astype(np.float32)
+
+
 def draw_activations_bf16(rng: np.random.Generator, m: int, hidden: int) -> np.ndarray:
     """x = bf16(N(0,1)) as uint16 bits [m, H]."""
     return bf16_bits_from_f32(rng.standard_normal((m, hidden)).astype(np.float32))
