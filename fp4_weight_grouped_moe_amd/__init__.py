@@ -43,6 +43,11 @@ class moe_w4a16_dims(ctypes.Structure):
                 ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32)]
 
 
+class moe_w4a16_source_layout(ctypes.Structure):
+    _fields_ = [("w13_up_first", ctypes.c_int32), ("global_scale_reciprocal", ctypes.c_int32),
+                ("scale_per_row", ctypes.c_int32)]
+
+
 class moe_route_pack_view(ctypes.Structure):
     _fields_ = [("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
                 ("sorted_route_ids", ctypes.c_void_p), ("block_expert", ctypes.c_void_p),
@@ -80,6 +85,7 @@ def _load():
         "moe_w4a16_set_path": (I32, [I32]),
         "moe_w4a16_set_decode_max_m": (I32, [I32]),
         "moe_router_topk": (I32, [P, I64, I32, I32, I32, I32, P, P, P]),
+        "moe_w4a16_prepare_layout": (I32, [PD, ctypes.POINTER(moe_w4a16_source_layout), P, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -92,7 +98,7 @@ _lib = _load()
 EXPORTED = ("moe_route_pack_token_capacity", "moe_route_pack_workspace_size", "moe_route_pack",
             "moe_w4a16_prepared_size", "moe_w4a16_prepare", "moe_w4a16_workspace_size", "moe_w4a16_fused",
             "moe_w4a16_fused_profiled", "moe_last_error", "moe_w4a16_set_path", "moe_w4a16_set_decode_max_m",
-            "moe_router_topk")
+            "moe_router_topk", "moe_w4a16_prepare_layout")
 
 
 def lib():
@@ -189,6 +195,13 @@ def moe_w4a16_fused_profiled(dims: moe_w4a16_dims, prepared, prepared_bytes: int
                                          _ptr(topk_ids), _ptr(topk_weights), topk, _ptr(expert_map),
                                          num_global_experts, token_capacity, _ptr(workspace), workspace_bytes,
                                          _ptr(out), _stream(stream), arr, len(events)), "moe_w4a16_fused_profiled")
+
+
+def moe_w4a16_prepare_layout(dims: moe_w4a16_dims, layout: moe_w4a16_source_layout, w13, s13, g13, w2, s2, g2,
+                             prepared, prepared_bytes: int, stream=None) -> None:
+    _check(_lib.moe_w4a16_prepare_layout(ctypes.byref(dims), ctypes.byref(layout) if layout is not None else None,
+                                         _ptr(w13), _ptr(s13), _ptr(g13), _ptr(w2), _ptr(s2), _ptr(g2),
+                                         _ptr(prepared), prepared_bytes, _stream(stream)), "moe_w4a16_prepare_layout")
 
 
 ROUTER_SCORING = {"softmax": 0, "sigmoid": 1}

@@ -205,7 +205,17 @@ int moe_w4a16_prepared_size(const moe_w4a16_dims* dims, size_t* bytes) {
 int moe_w4a16_prepare(const moe_w4a16_dims* dims, const uint8_t* w13, const uint8_t* s13, const float* g13,
                       const uint8_t* w2, const uint8_t* s2, const float* g2, void* prepared, size_t prepared_bytes,
                       hipStream_t stream) {
+  return moe_w4a16_prepare_layout(dims, nullptr, w13, s13, g13, w2, s2, g2, prepared, prepared_bytes, stream);
+}
+
+int moe_w4a16_prepare_layout(const moe_w4a16_dims* dims, const moe_w4a16_source_layout* layout, const uint8_t* w13,
+                             const uint8_t* s13, const float* g13, const uint8_t* w2, const uint8_t* s2, const float* g2,
+                             void* prepared, size_t prepared_bytes, hipStream_t stream) {
   if (int rc = check_dims(dims)) return rc;
+  moe_w4a16_source_layout lay{};
+  if (layout) lay = *layout;
+  if ((lay.w13_up_first & ~1) || (lay.global_scale_reciprocal & ~1) || (lay.scale_per_row & ~1))
+    return fail(MOE_ERR_INVALID_ARG, "source layout flags must be 0 or 1");
   if (!w13 || !s13 || !w2 || !s2) return fail(MOE_ERR_INVALID_ARG, "a weight or scale pointer is NULL");
   if (dims->fmt == MOE_FMT_NVFP4_E4M3_K16 && (!g13 || !g2))
     return fail(MOE_ERR_INVALID_ARG, "NVFP4 needs the global scales g13 and g2");
@@ -219,6 +229,9 @@ int moe_w4a16_prepare(const moe_w4a16_dims* dims, const uint8_t* w13, const uint
   pp.w13 = w13; pp.s13 = s13; pp.g13 = g13;
   pp.w2 = w2; pp.s2 = s2; pp.g2 = g2;
   pp.out = static_cast<uint8_t*>(prepared);
+  pp.w13_up_first = lay.w13_up_first;
+  pp.global_reciprocal = lay.global_scale_reciprocal;
+  pp.scale_per_row = lay.scale_per_row;
   return launch_status(launch_prepare(pp, stream), "prepare launch");
 }
 

@@ -22,6 +22,12 @@ __device__ __forceinline__ int64_t fc1_row(const PreparedGeom& g, int64_t rg, in
   return i < g.I ? i : -1;
 }
 
+// Source row of canonical FC1 row `row` (up-half-first checkpoints swap the halves).
+__device__ __forceinline__ int64_t fc1_src_row(const PrepareParams& p, int64_t row) {
+  if (row < 0 || !p.w13_up_first || p.g.act != ACT_SWIGLU) return row;
+  return row < p.g.I ? row + p.g.I : row - p.g.I;
+}
+
 __device__ __forceinline__ int64_t fc2_row(const PreparedGeom& g, int64_t rg, int r) {
   int64_t i = rg * kRowGroup + r;
   return i < g.H ? i : -1;
@@ -57,7 +63,7 @@ __global__ void prepare_nibbles_kernel(PrepareParams p) {
     const int64_t rg = rest % groups;
     const int64_t e = rest / groups;
     const int r = lane & 15;
-    const int64_t row = FC1 ? fc1_row(g, rg, r) : fc2_row(g, rg, r);
+    const int64_t row = FC1 ? fc1_src_row(p, fc1_row(g, rg, r)) : fc2_row(g, rg, r);
     const int64_t k0 = kb * kKBlock + 32 * s + 8 * (lane >> 4);
     uint32_t v = 0;
     if (row >= 0) v = gather_codes(src + (e * rows_src + row) * (K / 2), K, k0);
@@ -75,7 +81,8 @@ __global__ void prepare_scales_kernel(PrepareParams p) {
   const int64_t rows_src = FC1 ? (g.act == ACT_SWIGLU ? 2 * g.I : g.I) : g.H;
   const bool nv = g.fmt == FMT_NVFP4;
   const int64_t G = nv ? 16 : 32;
-  const int64_t ngroups_src = (K + G - 1) / G;
+  const int64_t ngroups = (K + G - 1) / G;                 // scale groups along K
+  const int64_t ngroups_src = p.scale_per_row ? 1 : ngroups;   // stored per row
   const uint8_t* src = FC1 ? p.s13 : p.s2;
   uint8_t* dst = p.out + (FC1 ? g.off_sc1 : g.off_sc2);
   const uint8_t pad = nv ? 0 : 127;   // E4M3 0 or E8M0 2^0: finite, and the padded codes are 0
@@ -92,9 +99,9 @@ __global__ void prepare_scales_kernel(PrepareParams p) {
     const int64_t kb = chunk * kScaleChunkKB + kbm;
     const int64_t grp = nv ? 8 * kb + 2 * s + h : 4 * kb + s;
     const int64_t rg = eg % groups, e = eg / groups;
-    const int64_t row = FC1 ? fc1_row(g, rg, r) : fc2_row(g, rg, r);
+    const int64_t row = FC1 ? fc1_src_row(p, fc1_row(g, rg, r)) : fc2_row(g, rg, r);
     uint8_t v = pad;
-    if (row >= 0 && kb < kbs && grp < ngroups_src) v = src[(e * rows_src + row) * ngroups_src + grp];
+    if (row >= 0 && kb < kbs && grp < ngroups) v = src[(e * rows_src + row) * ngroups_src + (p.scale_per_row ? 0 : grp)];
     dst[i] = v;
   }
 }
@@ -105,8 +112,9 @@ __global__ void prepare_globals_kernel(PrepareParams p) {
   float* d2 = reinterpret_cast<float*>(p.out + g.off_g2);
   for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < g.E; e += gridDim.x * blockDim.x) {
     const bool nv = g.fmt == FMT_NVFP4;
-    d13[e] = nv ? p.g13[e] : 1.0f;
-    d2[e] = nv ? p.g2[e] : 1.0f;
+    // encode-sense globals: the correctly rounded fp32 quotient 1 / stored
+    d13[e] = nv ? (p.global_reciprocal ? __fdiv_rn(1.0f, p.g13[e]) : p.g13[e]) : 1.0f;
+    d2[e] = nv ? (p.global_reciprocal ? __fdiv_rn(1.0f, p.g2[e]) : p.g2[e]) : 1.0f;
   }
 }
 

@@ -135,6 +135,30 @@ int moe_w4a16_prepare(const moe_w4a16_dims* dims, const uint8_t* w13, const uint
                       const float* g13, const uint8_t* w2, const uint8_t* s2, const float* g2,
                       void* prepared, size_t prepared_bytes, hipStream_t stream);
 
+/* Source layouts other than the canonical one (page: Summary, ModelOpt / CompressedTensors
+ * formats; Walkthrough, weight format preparation and layout normalisation; review of the
+ * preparation module, single-scale branch). Each flag is 0 (canonical) or 1:
+ *   w13_up_first             SwiGLU W13 rows [0, I) are up and [I, 2I) gate (s13 likewise);
+ *                            ignored for relu2.
+ *   global_scale_reciprocal  NVFP4 g13 / g2 hold the encode scale 1/g; the prepared buffer
+ *                            keeps the correctly rounded fp32 quotient 1/stored. Ignored for
+ *                            MXFP4.
+ *   scale_per_row            s13 is [E, N1, 1] and s2 [E, H, 1]: one scale byte per row for
+ *                            all of K (group size -1).
+ * The prepared buffer equals, byte for byte, the one moe_w4a16_prepare makes from the
+ * canonical arrays these describe. layout may be NULL (canonical). Errors as for
+ * moe_w4a16_prepare, plus MOE_ERR_INVALID_ARG for a flag outside {0, 1}. */
+typedef struct moe_w4a16_source_layout {
+  int32_t w13_up_first;
+  int32_t global_scale_reciprocal;
+  int32_t scale_per_row;
+} moe_w4a16_source_layout;
+
+int moe_w4a16_prepare_layout(const moe_w4a16_dims* dims, const moe_w4a16_source_layout* layout,
+                             const uint8_t* w13, const uint8_t* s13, const float* g13, const uint8_t* w2,
+                             const uint8_t* s2, const float* g2, void* prepared, size_t prepared_bytes,
+                             hipStream_t stream);
+
 /* ------------------------------------------------------------------ the fused layer
  * Page: Description (fused FC1/FC2 kernel with cooperative persistent launches; a
  * small-batch decode path that folds the top-k sum into the FC2 store epilogue),

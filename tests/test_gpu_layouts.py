@@ -1,0 +1,94 @@
+"""Preparation from the source-layout variants (GPU): the prepared buffer equals, byte for
+byte, the one prepared from the canonical arrays that the oracle maps the variant to."""
+
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import layouts as L
+from synth import draw as D
+
+from _common import SCALED
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def device():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    d = torch.device("cuda:0")
+    torch.cuda.set_device(d)
+    return d
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import fp4_weight_grouped_moe_amd as m
+
+    return m
+
+
+def _variant(cfg, seed, up_first, reciprocal, per_row):
+    """A source-layout variant drawn at random: (w13, s13, g13, w2, s2, g2) as stored."""
+    codes = D.draw_random_codes(cfg, seed)
+    w13, s13, g13, w2, s2, g2 = (codes[k] for k in ("w13", "s13", "g13", "w2", "s2", "g2"))
+    if per_row:
+        s13 = np.ascontiguousarray(s13[:, :, :1])
+        s2 = np.ascontiguousarray(s2[:, :, :1])
+    if up_first and cfg.act == "silu_swiglu":
+        w13 = L.w13_gate_first(w13, cfg.inter)          # the swap is its own inverse
+        s13 = L.w13_gate_first(s13, cfg.inter)
+    if reciprocal and cfg.fmt == "nvfp4":
+        g13 = (np.float32(1) / np.asarray(g13, np.float32)).astype(np.float32)
+        g2 = (np.float32(1) / np.asarray(g2, np.float32)).astype(np.float32)
+    return w13, s13, g13, w2, s2, g2
+
+
+def _prepare(moe, device, cfg, arrays, layout):
+    import torch
+
+    dims = moe.make_dims(cfg.fmt, cfg.act, cfg.num_experts, cfg.hidden, cfg.inter)
+    size = moe.moe_w4a16_prepared_size(dims)
+    out = torch.full((size,), 0xA5, dtype=torch.uint8, device=device)
+    t = [torch.from_numpy(np.ascontiguousarray(a)).to(device) if a is not None else None for a in arrays]
+    if cfg.fmt != "nvfp4":
+        t[2] = t[5] = None
+    if layout is None:
+        moe.moe_w4a16_prepare(dims, t[0], t[1], t[2], t[3], t[4], t[5], out, size)
+    else:
+        moe.moe_w4a16_prepare_layout(dims, layout, t[0], t[1], t[2], t[3], t[4], t[5], out, size)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["decode_s", "small_s", "edge_s"])
+@pytest.mark.parametrize("up_first,reciprocal,per_row", list(itertools.product([0, 1], repeat=3))[1:])
+def test_prepare_layout_equals_canonical(moe, device, name, up_first, reciprocal, per_row):
+    cfg = SCALED[name]
+    print(f"layout {name} up_first={up_first} reciprocal={reciprocal} per_row={per_row}", flush=True)
+    var = _variant(cfg, 77 + 8 * up_first + 4 * reciprocal + 2 * per_row, up_first, reciprocal, per_row)
+    canon = L.canonical(cfg.fmt, cfg.act, cfg.hidden, cfg.inter, *var, w13_up_first=bool(up_first),
+                        global_scale_reciprocal=bool(reciprocal), scale_per_row=bool(per_row))
+    layout = moe.moe_w4a16_source_layout(up_first, reciprocal, per_row)
+    got = _prepare(moe, device, cfg, var, layout)
+    want = _prepare(moe, device, cfg, canon, None)
+    assert got.shape == want.shape
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} prepared bytes differ, first at {bad[:8]}"
+
+
+def test_prepare_layout_rejects_bad_flags(moe, device):
+    import torch
+
+    cfg = SCALED["decode_s"]
+    dims = moe.make_dims(cfg.fmt, cfg.act, cfg.num_experts, cfg.hidden, cfg.inter)
+    size = moe.moe_w4a16_prepared_size(dims)
+    buf = torch.empty(size, dtype=torch.uint8, device=device)
+    with pytest.raises(moe.MoeError):
+        moe.moe_w4a16_prepare_layout(dims, moe.moe_w4a16_source_layout(2, 0, 0), buf, buf, buf, buf, buf, buf, buf, size)
