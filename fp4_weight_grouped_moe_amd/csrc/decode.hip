@@ -12,10 +12,14 @@
 //    time; its K blocks are dealt to the waves in slices, partial sums meet in LDS, and
 //    wave 0 applies the FC1 global scale, the activation, the router weight and the FC2
 //    global scale and stores the bf16 row slice of each route. The activation rows of
-//    all m tokens sit in LDS.
-//  * FC2: a workgroup (16 waves) owns 16 hidden rows for every route block; each unit's
-//    route results are added into per-wave, per-token LDS sums (the top-k sum), which are
-//    reduced in a fixed order and stored once as bf16 -- deterministic, no global atomics.
+//    all m tokens sit in LDS, staged by DMA.
+//  * FC2 (K split): a workgroup owns a few hidden row groups and one pair of intermediate
+//    K blocks for every route block, with that K slice of every route staged in LDS; route
+//    results go into per-wave, per-token LDS sums (the top-k sum), and the last K split of
+//    a row group to finish adds the splits in a fixed order and stores bf16 once --
+//    deterministic, no atomics on data.
+//  * FC2 (one pass, when the staged rows do not fit): a workgroup (16 waves) owns 16 hidden
+//    rows for every route block and full K, with the same per-token LDS sums.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -32,21 +36,6 @@ constexpr int kF1Slice = 4;          // K blocks per FC1 unit
 constexpr int kF2Threads = 1024;
 constexpr int kF2Waves = kF2Threads / 64;
 constexpr int kF2Slice = 2;          // K blocks per FC2 unit
-
-__device__ __forceinline__ uint32_t scale_dword(const uint8_t* sc_group, int64_t kb, int lane, bool nv) {
-  // Scales of K block kb for this lane: NVFP4 chunk [h][row][kb%4][s], MXFP4 [row][kb%4][s].
-  const int r = lane & 15;
-  const int64_t chunk = kb >> 2;
-  const int sub = int(kb & 3);
-  const int64_t off = nv ? chunk * 512 + ((lane >> 5) * 16 + r) * 16 + sub * 4 : chunk * 256 + r * 16 + sub * 4;
-  return *reinterpret_cast<const uint32_t*>(sc_group + off);
-}
-
-// 16-byte chunk j of LDS row `row` is stored at chunk j ^ (row & 7) inside every complete
-// group of 8 chunks, so lanes reading the same K of different rows hit different banks.
-__device__ __forceinline__ int64_t swz(int64_t j, int row, int64_t chunks_per_row) {
-  return ((j | 7) < chunks_per_row) ? (j ^ (row & 7)) : j;
-}
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

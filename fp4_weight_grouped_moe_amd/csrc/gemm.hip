@@ -31,7 +31,6 @@ namespace moe {
 namespace {
 
 constexpr int kGemmThreads = 512;                       // 8 waves, two per SIMD
-constexpr int kGemmWaves = kGemmThreads / 64;
 constexpr int kRowBytes = kKBlock * 2;                  // one activation row of a K block: 256 B
 constexpr int kBlockBytes = kBlockM * kRowBytes;        // one route block of a K block: 4 KiB
 constexpr int kLdsBytes = 131072;                       // the activation stage ring
