@@ -214,21 +214,27 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
       return __builtin_bit_cast(T, *reinterpret_cast<const u32x4*>((s & 1 ? xb_odd : xb_even) + b * kBlockBytes +
                                                                    (s >> 1) * 256));
     };
-    // Two waves share each SIMD, so LDS latency is hidden by the other wave: the activation
-    // fragments of a K-step are read just before its MFMAs (no double buffer, no spills).
+    // The activation fragments of K-step s + 1 are read while K-step s runs its MFMAs (two
+    // register sets inside the stage; the first K-step's reads wait at the stage start).
+    // The scheduling barrier after each K-step keeps the compiler from hoisting further
+    // reads (register pressure).
+    T xb2[2][BW];
+#pragma unroll
+    for (int b = 0; b < BW; ++b) xb2[0][b] = xread(b, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       issue_part(s, kb_next, slot_next, wd_next, scd_next);
-      T xb[BW], a[FR];
+      if (s < 3) {
 #pragma unroll
-      for (int b = 0; b < BW; ++b) xb[b] = xread(b, s);
+        for (int b = 0; b < BW; ++b) xb2[(s + 1) & 1][b] = xread(b, s + 1);
+      }
+      T a[FR];
 #pragma unroll
       for (int f = 0; f < FR; ++f) a[f] = dq[f](wq[f][s], s);
 #pragma unroll
       for (int b = 0; b < BW; ++b)
 #pragma unroll
-        for (int f = 0; f < FR; ++f) acc[f][b] = mma(a[f], xb[b], acc[f][b]);
-      // Keep the scheduler from hoisting the next K-steps' reads (register pressure).
+        for (int f = 0; f < FR; ++f) acc[f][b] = mma(a[f], xb2[s & 1][b], acc[f][b]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
