@@ -309,9 +309,12 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   rp.route_slot = reinterpret_cast<int32_t*>(pk + pg.off_route_slot);
   rp.tiles = decode ? nullptr : reinterpret_cast<int2*>(pk + pg.off_tiles);   // M tiles: grouped GEMM only
   rp.slot_info = reinterpret_cast<int2*>(pk + pg.off_tok_of_slot);
+  // At small m the decode FC1 launch packs the routes itself (no route-pack launch) and
+  // converts the activation rows in LDS.
+  const bool fc1_packs = decode && decode_fc1_packs(g, m, topk);
   // NVFP4 weights run on the f16 MFMA wherever the activations are staged whole: the grouped
   // GEMM always, the decode path when its rows fit in LDS.
-  const bool convert = dims->fmt == MOE_FMT_NVFP4_E4M3_K16 && (!decode || decode_stages_x(g, m));
+  const bool convert = dims->fmt == MOE_FMT_NVFP4_E4M3_K16 && !fc1_packs && (!decode || decode_stages_x(g, m));
   rp.x = x;
   rp.x16 = convert ? reinterpret_cast<uint16_t*>(ws + fg.off_x16) : nullptr;
   rp.xexp = convert ? reinterpret_cast<int32_t*>(ws + fg.off_xexp) : nullptr;
@@ -343,12 +346,20 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   fp.part = reinterpret_cast<float*>(ws + fg.off_part);
   fp.f2_count = decode ? reinterpret_cast<int32_t*>(ws + fg.off_count) : nullptr;
   fp.cap_blocks = pg.cap_blocks;
+  if (fc1_packs) {
+    fp.topk_ids = topk_ids;
+    fp.topk_weights = topk_weights;
+    fp.expert_map = expert_map;
+    fp.num_global_experts = num_global_experts;
+  }
 
   if (events) (void)hipEventRecord(events[0], stream);
   // extra route-pack workgroups for the conversion: one wave per row, 16 waves each
   const int side_blocks = decode ? int((m + 15) / 16) : cus;
-  if (hipError_t e = launch_route_pack(rp, side_blocks, stream); e != hipSuccess)
-    return launch_status(e, "route pack launch");
+  if (!fc1_packs) {
+    if (hipError_t e = launch_route_pack(rp, side_blocks, stream); e != hipSuccess)
+      return launch_status(e, "route pack launch");
+  }
   if (events) (void)hipEventRecord(events[1], stream);
   hipEvent_t* marks = events ? events + 2 : nullptr;
   hipError_t e = decode ? launch_decode(fp, cus, stream, marks) : launch_gemm(fp, cus, stream, marks);

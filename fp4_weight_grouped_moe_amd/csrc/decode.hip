@@ -36,8 +36,35 @@ constexpr int kF1Slice = 4;          // K blocks per FC1 unit
 constexpr int kF2Threads = 1024;
 constexpr int kF2Waves = kF2Threads / 64;
 constexpr int kF2Slice = 2;          // K blocks per FC2 unit
+constexpr int kF1PackRoutes = 256;   // FC1 packs the routes itself up to this many (one per thread)
+constexpr int kF1PackExperts = 2048; // and this many local experts (their counts share the partial-sum area)
+constexpr int kF1StaticLds = 2 * (kF1Waves - 1) * 2 * 64 * 16;   // the partial-sum area
+constexpr int kLdsPerCU = 163840;
+static_assert(kF1PackRoutes == kF1Threads, "one route per thread");
+
+// Route blocks the pack of R routes over E experts can produce: at most one per route, and
+// at most one per touched expert plus R / 16 more.
+__host__ __device__ inline int f1_pack_blocks(int routes, int E) {
+  const int t = routes < E ? routes : E;
+  const int b = t + (routes + kBlockM - 1) / kBlockM;
+  return routes < b ? routes : b;
+}
+// LDS of the pack tables: slot -> route (int16), block -> expert, route -> weight, token (int16).
+__host__ __device__ inline size_t f1_pack_lds_bytes(int routes, int E) {
+  const int nb = f1_pack_blocks(routes, E);
+  return size_t(nb) * kBlockM * 2 + size_t(nb) * 4 + size_t(routes) * 4 + (size_t(routes) * 2 + 15) / 16 * 16;
+}
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Workgroup barrier over LDS only: this wave's LDS operations have completed (lgkmcnt 0),
+// while its loads into LDS by DMA may still be in flight (a release fence would wait for
+// them too).
+__device__ __forceinline__ void pack_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // ----------------------------------------------------------------------------- FC1
 
@@ -49,54 +76,177 @@ struct F1Unit {
   int2 info;                         // (token, router weight) of this lane's route column
 };
 
-template <int FMT, bool STAGED>
+template <int FMT, bool STAGED, bool PACK>
 __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p) {
   extern __shared__ __align__(16) uint8_t dyn[];
   // Partial sums of waves 1..3 for the item epilogue, double-buffered by item parity so that
   // one barrier per item suffices: a wave refills a buffer only after the next item's
-  // barrier, which wave 0 reaches only after it has read that buffer.
+  // barrier, which wave 0 reaches only after it has read that buffer. The route pack (PACK)
+  // uses the same area for its counts before the first item.
   __shared__ f32x4 red[2][kF1Waves - 1][2][64];
+  static_assert(sizeof(red) >= (kF1PackExperts + 16) * 4 + kF1PackRoutes * 2, "pack scratch fits the partial-sum area");
   const PreparedGeom& g = p.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
   const int q = lane >> 4, col = lane & 15;
   const int H = g.H;
   const int xp = int(p.xs_pitch);                            // elements per staged row
-  const int live_blocks = p.live[2];
   uint16_t* xs = reinterpret_cast<uint16_t*>(dyn);           // [m][xp], chunk-swizzled
   int* sp = reinterpret_cast<int*>(dyn + size_t(p.m) * xp * 2);   // [64] per-token exponent p
+  // PACK: the route tables after the exponents (f1_pack_lds_bytes).
+  const int R = int(p.m) * p.topk;
+  const int nbmax = f1_pack_blocks(R, g.E);
+  int16_t* sroute = reinterpret_cast<int16_t*>(dyn + size_t(p.m) * xp * 2 + 256);   // [nbmax * 16] slot -> route
+  int* sbe = reinterpret_cast<int*>(sroute + nbmax * kBlockM);                       // [nbmax] block -> expert
+  float* sw = reinterpret_cast<float*>(sbe + nbmax);                                 // [R] router weight
+  int16_t* stk = reinterpret_cast<int16_t*>(sw + R);                                 // [R] token
 
   const int n_it = int(g.n1_groups / 2);                      // items per block: two row groups
-  const int n_items = live_blocks * n_it;
   const int nsl = int((g.kb1 + kF1Slice - 1) / kF1Slice);     // K slices per item
   const int spw = (nsl + kF1Waves - 1) / kF1Waves;            // slices per wave per item
-  const int my_items = n_items > int(blockIdx.x) ? (n_items - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x) : 0;
-  const int U = my_items * spw;
-  const int U2 = (U + 1) & ~1;                                // even: units are taken in pairs
   const int kb1 = int(g.kb1);
   const int sc_lane = FMT == FMT_NVFP4 ? ((lane >> 5) * 16 + col) * 16 : col * 16;
   // FC2's per-group arrival counts start at zero in every call.
   if (blockIdx.x == 0 && p.f2_count)
     for (int i = tid; i < int(g.n2_groups); i += kF1Threads) p.f2_count[i] = 0;
-  if (U == 0) return;
+  int live_blocks = PACK ? 0 : p.live[2];
+  if (!PACK && live_blocks * n_it <= int(blockIdx.x)) return;   // no item for this workgroup
 
-  // NVFP4 runs on the f16 MFMA: E2M1 x E4M3 weights are exact in f16, and the route-pack
-  // launch stored each token's row times a power of two 2^-p (exact) with its largest
-  // magnitude in [2^14, 2^15) as f16; the epilogue multiplies by 2^p again.
+  // NVFP4 runs on the f16 MFMA: E2M1 x E4M3 weights are exact in f16, and each token's row
+  // is staged times a power of two 2^-p (exact) with its largest magnitude in [2^14, 2^15)
+  // as f16 (converted by the route-pack launch, or here in LDS when this launch packs); the
+  // epilogue multiplies by 2^p again.
   constexpr bool F16 = STAGED && FMT == FMT_NVFP4;
   if constexpr (STAGED) {
     // Activation rows into LDS by DMA, zero-padded to xp. Chunk j of row t sits at chunk
     // j ^ (t & 7) (hp is a multiple of 128, so every group of 8 chunks is complete): lanes
     // reading the same K of different tokens hit different banks. Lane i of a DMA row writes
     // LDS chunk 64c + i, so it fetches source chunk (64c + i) ^ (t & 7).
-    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(F16 ? p.x16 : p.x, uint32_t(p.m * H * 2));
+    // PACK: waves 1..3 stage the rows while wave 0 loads the routes (the pack waits on no DMA).
+    const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(F16 && !PACK ? p.x16 : p.x, uint32_t(p.m * H * 2));
     const int per_row = xp / 512;
-    for (int n = wave; n < int(p.m) * per_row; n += kF1Waves) {
+    constexpr int kDmaWaves = PACK ? kF1Waves - 1 : kF1Waves;
+    for (int n = PACK ? wave - 1 : wave; n >= 0 && n < int(p.m) * per_row; n += kDmaWaves) {
       const int t = n / per_row, c = n % per_row;
       const int j = (64 * c + lane) ^ (t & 7);
       dma16(xr, reinterpret_cast<const uint8_t*>(xs + t * xp + 512 * c), j * 8 < H ? uint32_t(t * H * 2 + j * 16) : kOutOfRange);
     }
-    if (F16 && wave == 0) dma4(buffer_rsrc(p.xexp, uint32_t(p.m * 4)), sp, uint32_t(lane * 4));
+    if (F16 && !PACK && wave == 0) dma4(buffer_rsrc(p.xexp, uint32_t(p.m * 4)), sp, uint32_t(lane * 4));
   }
+
+  if constexpr (PACK) {
+    // The route pack of these few routes (R <= 256, one per thread), done by every workgroup
+    // in its own LDS so that no launch waits for another: local expert ids, counts, padded
+    // segment offsets (exclusive scan over the experts), block -> expert, and stable slots
+    // (rank among the lower routes of the same expert), exactly as the route-pack kernel
+    // orders them. Workgroup 0 also writes the tables FC2 reads.
+    int* cnt = reinterpret_cast<int*>(&red[0][0][0][0]);     // [E] counts, then offsets
+    int* scr = cnt + kF1PackExperts;                          // [16] scan scratch
+    int16_t* sl = reinterpret_cast<int16_t*>(scr + 16);       // [256] local expert ids (-1 past R)
+    // Barriers here order LDS only (lgkmcnt, no release fence): waves 1..3 keep their row
+    // DMA in flight until the wait before the last one.
+    for (int e = tid; e < g.E; e += kF1Threads) cnt[e] = 0;
+    for (int s = tid; s < nbmax * kBlockM; s += kF1Threads) sroute[s] = -1;
+    if (wave == 0) {
+      int gid[kF1PackRoutes / 64];
+      float wt[kF1PackRoutes / 64];
+#pragma unroll
+      for (int i = 0; i < kF1PackRoutes / 64; ++i) {
+        const int r = lane + 64 * i;
+        gid[i] = r < R ? p.topk_ids[r] : -1;
+        wt[i] = r < R ? p.topk_weights[r] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < kF1PackRoutes / 64; ++i) {
+        const int r = lane + 64 * i;
+        int l = -1;
+        if (gid[i] >= 0 && gid[i] < p.num_global_experts) {
+          const int v = p.expert_map ? p.expert_map[gid[i]] : gid[i];
+          l = (v >= 0 && v < g.E) ? v : -1;
+        }
+        sl[r] = int16_t(l);
+        if (r < R) {
+          sw[r] = wt[i];
+          stk[r] = int16_t(r / p.topk);
+        }
+      }
+    }
+    pack_barrier();
+    const int l = sl[tid];
+    if (l >= 0) atomicAdd(&cnt[l], 1);
+    pack_barrier();
+    constexpr int kPer = kF1PackExperts / kF1Threads;
+    const int e0 = tid * kPer;
+    int c[kPer], padded = 0, valid = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      c[i] = e0 + i < g.E ? cnt[e0 + i] : 0;
+      padded += (c[i] + kBlockM - 1) / kBlockM * kBlockM;
+      valid += c[i];
+    }
+    int x = padded, vx = valid;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64), vy = __shfl_up(vx, d, 64);
+      if (lane >= d) { x += y; vx += vy; }
+    }
+    if (lane == 63) { scr[wave] = x; scr[kF1Waves + wave] = vx; }
+    pack_barrier();
+    int off = x - padded, total = 0, nvalid = 0;
+#pragma unroll
+    for (int w = 0; w < kF1Waves; ++w) {
+      off += w < wave ? scr[w] : 0;
+      total += scr[w];
+      nvalid += scr[kF1Waves + w];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (e0 + i < g.E) {
+        cnt[e0 + i] = off;                                    // only this thread read these counts
+        const int pb = (c[i] + kBlockM - 1) / kBlockM;
+        for (int b = 0; b < pb; ++b) sbe[off / kBlockM + b] = e0 + i;
+        off += pb * kBlockM;
+      }
+    }
+    pack_barrier();
+    if (l >= 0) {
+      int rank = 0;
+      for (int j = 0; j < R; j += 8) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(sl + j);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int li = int(int16_t(v[i >> 1] >> (16 * (i & 1))));
+          rank += (j + i < tid) & (li == l);
+        }
+      }
+      const int slot = cnt[l] + rank;
+      sroute[slot] = int16_t(tid);
+      if (blockIdx.x == 0) p.route_slot[tid] = slot;
+    } else if (tid < R && blockIdx.x == 0) {
+      p.route_slot[tid] = -1;
+    }
+    wait_vmcnt<0>();                                          // the rows (waves 1..3) have landed
+    pack_barrier();
+    live_blocks = total / kBlockM;
+    if (blockIdx.x == 0) {
+      for (int s = tid; s < live_blocks * kBlockM; s += kF1Threads) {
+        const int r = sroute[s];
+        p.sorted_route_ids[s] = r;
+        p.slot_info[s] = make_int2(r >= 0 ? int(stk[r]) : -1, r >= 0 ? __float_as_int(sw[r]) : 0);
+      }
+      for (int b = tid; b < live_blocks; b += kF1Threads) p.block_expert[b] = sbe[b];
+      if (tid == 0) {
+        p.live[0] = nvalid;
+        p.live[1] = total;
+        p.live[2] = live_blocks;
+        p.live[3] = int(p.m);
+      }
+    }
+    if (live_blocks * n_it <= int(blockIdx.x)) return;        // no item for this workgroup
+  }
+  const int n_items = live_blocks * n_it;
+  const int my_items = (n_items - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
+  const int U = my_items * spw;
+  const int U2 = (U + 1) & ~1;                                // even: units are taken in pairs
 
   // Loads are unconditional so that the wait counters stay exact: units past the end and
   // K blocks past kb1 re-read a valid block (an L2 hit) whose contribution is skipped.
@@ -107,8 +257,16 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
     const int item = int(blockIdx.x) + (uu / spw) * int(gridDim.x);
     const int sl = min(wave + kF1Waves * (uu % spw), nsl - 1);
     const int blk = item / n_it, it = item % n_it;
-    r.info = p.slot_info[blk * kBlockM + col];
-    const int64_t gi = int64_t(scalar_load(p.block_expert, blk)) * g.n1_groups + 2 * it;
+    int eb;
+    if constexpr (PACK) {
+      const int rr = sroute[blk * kBlockM + col];
+      r.info = make_int2(rr >= 0 ? int(stk[rr]) : -1, rr >= 0 ? __float_as_int(sw[rr]) : 0);
+      eb = uniform(sbe[blk]);
+    } else {
+      r.info = p.slot_info[blk * kBlockM + col];
+      eb = scalar_load(p.block_expert, blk);
+    }
+    const int64_t gi = int64_t(eb) * g.n1_groups + 2 * it;
     const uint8_t* nb0 = p.nib1 + gi * g.kb1 * kFragBytes;
     const uint8_t* nb1 = nb0 + g.kb1 * kFragBytes;
 #pragma unroll
@@ -127,7 +285,37 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
   F1Unit ra, rb;
   issue(0, ra);
   issue(1, rb);
-  if constexpr (STAGED) wait_vmcnt<0>();
+  if constexpr (PACK && F16) {
+    // The bf16 rows (landed before the pack's last barrier) to f16 times 2^-p in place, one
+    // wave per row, while the first units' weights are in flight.
+    const int nch = xp / 8;
+    for (int t = wave; t < int(p.m); t += kF1Waves) {
+      u32x4* row = reinterpret_cast<u32x4*>(xs + t * xp);
+      float mx = 0.f;
+      for (int c = lane; c < nch; c += 64) {
+        const u32x4 v = row[c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(v[i] << 16)), fabsf(__uint_as_float(v[i] & 0xFFFF0000u))));
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+      const int pe = (mx > 0.f && mx <= 3.4e38f) ? __builtin_amdgcn_frexp_expf(mx) - 15 : 0;
+      for (int c = lane; c < nch; c += 64) {
+        const u32x4 v = row[c];
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f16x2 h = f16x2{(_Float16)ldexpf(__uint_as_float(v[i] << 16), -pe),
+                                (_Float16)ldexpf(__uint_as_float(v[i] & 0xFFFF0000u), -pe)};
+          o[i] = __builtin_bit_cast(uint32_t, h);
+        }
+        row[c] = o;
+      }
+      if (lane == 0) sp[t] = pe;
+    }
+  }
+  if constexpr (STAGED && !PACK) wait_vmcnt<0>();
   lds_barrier();
 
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -173,7 +361,7 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
     const int item = int(blockIdx.x) + (u / spw) * int(gridDim.x);
     const int blk = item / n_it, it = item % n_it;
     const int par = (u / spw) & 1;
-    const int e = scalar_load(p.block_expert, blk);
+    const int e = PACK ? uniform(sbe[blk]) : scalar_load(p.block_expert, blk);
     float g13 = scalar_load(p.g13, e);
     const float g2 = scalar_load(p.g2, e);
     if (wave != 0) {
@@ -576,8 +764,9 @@ hipError_t allow_lds(K kernel, int bytes) {
 template <int FMT>
 hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t stream, hipEvent_t* marks) {
   static const hipError_t lds_ok = [] {
-    // dynamic LDS: FC1 staged rows + exponents; FC2 block table + slot tokens
-    hipError_t e = allow_lds(&decode_fc1_kernel<FMT, true>, kDecodeStageBytes + 256);
+    // dynamic LDS: FC1 staged rows + exponents (+ pack tables); FC2 block table + slot tokens
+    hipError_t e = allow_lds(&decode_fc1_kernel<FMT, true, false>, kDecodeStageBytes + 256);
+    if (e == hipSuccess) e = allow_lds(&decode_fc1_kernel<FMT, true, true>, kLdsPerCU - kF1StaticLds);
     if (e == hipSuccess) e = allow_lds(&decode_fc2_kernel<FMT>, 98304);
     if (e == hipSuccess) e = allow_lds(&decode_fc2_split_kernel<FMT, kF3RowGroups>, kF3MaxLds);
     return e;
@@ -587,12 +776,16 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
   const PreparedGeom& g = p.g;
   p.xs_pitch = decode_x_pitch(g);
   const int64_t items = p.cap_blocks * (g.n1_groups / 2);
-  const bool two_per_cu = p.m * p.xs_pitch * 2 <= kDecodeStageTwoPerCU;   // else the LDS holds one workgroup
+  const bool pack = p.topk_ids != nullptr;                     // FC1 packs the routes (decode_fc1_packs)
+  const size_t lds1 = size_t(p.m) * p.xs_pitch * 2 + 256 + (pack ? f1_pack_lds_bytes(int(p.m) * p.topk, g.E) : 0);
+  const bool two_per_cu = 2 * (lds1 + kF1StaticLds) <= size_t(kLdsPerCU);   // else the LDS holds one workgroup
   const int64_t grid1 = max(int64_t(1), min(items, int64_t(num_cus) * (two_per_cu ? 2 : 1)));
-  if (decode_stages_x(g, p.m))
-    hipLaunchKernelGGL((decode_fc1_kernel<FMT, true>), dim3(grid1), dim3(kF1Threads), size_t(p.m) * p.xs_pitch * 2 + 256, stream, p);
+  if (pack)
+    hipLaunchKernelGGL((decode_fc1_kernel<FMT, true, true>), dim3(grid1), dim3(kF1Threads), lds1, stream, p);
+  else if (decode_stages_x(g, p.m))
+    hipLaunchKernelGGL((decode_fc1_kernel<FMT, true, false>), dim3(grid1), dim3(kF1Threads), lds1, stream, p);
   else
-    hipLaunchKernelGGL((decode_fc1_kernel<FMT, false>), dim3(grid1), dim3(kF1Threads), 0, stream, p);
+    hipLaunchKernelGGL((decode_fc1_kernel<FMT, false, false>), dim3(grid1), dim3(kF1Threads), 0, stream, p);
   if (marks) (void)hipEventRecord(marks[0], stream);
   constexpr int RG = kF3RowGroups;
   const size_t lds3 = f3_lds_bytes<RG>(p.m, p.topk, p.cap_blocks);
@@ -618,6 +811,16 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
 }
 
 }  // namespace
+
+bool decode_fc1_packs(const PreparedGeom& g, int64_t m, int topk) {
+  // Only while two FC1 workgroups still fit on a CU: with one (more staged rows) the
+  // separate route-pack launch, which also converts the rows once, was measured faster
+  // (small shape, m = 16: 127.8 against 129.1 us per layer).
+  const int64_t routes = m * topk;
+  return m >= 1 && routes <= kF1PackRoutes && g.E <= kF1PackExperts && decode_stages_x(g, m) &&
+         2 * (size_t(m) * decode_x_pitch(g) * 2 + 256 + f1_pack_lds_bytes(int(routes), g.E) + kF1StaticLds) <=
+             size_t(kLdsPerCU);
+}
 
 hipError_t launch_decode(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks) {
   return p.g.fmt == FMT_NVFP4 ? launch_decode_fmt<FMT_NVFP4>(p, num_cus, stream, marks)

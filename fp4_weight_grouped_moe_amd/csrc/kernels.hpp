@@ -58,12 +58,18 @@ struct FusedParams {
   uint16_t* out;                 // bf16 [m, H]
   int64_t m;
   int32_t topk;
-  const int32_t* sorted_route_ids;
-  const int32_t* block_expert;
+  int32_t* sorted_route_ids;
+  int32_t* block_expert;
   int32_t* live;                 // route-pack counts; [8..15] FC1, [16..23] FC2 work queues
   const int2* tiles;
-  const int2* slot_info;
-  const int32_t* route_slot;      // [m * topk] packed slot of each route or -1
+  int2* slot_info;
+  int32_t* route_slot;           // [m * topk] packed slot of each route or -1
+  // Decode FC1 packing the routes itself (no route-pack launch): its inputs. Workgroup 0
+  // writes the tables above that FC2 reads.
+  const int32_t* topk_ids;       // [m * topk]
+  const float* topk_weights;     // [m * topk]
+  const int32_t* expert_map;     // [num_global_experts] or null
+  int32_t num_global_experts;
   uint16_t* inter;               // bf16 [cap_routes, ip]
   const uint16_t* x16;           // f16 [m, H] scaled activations (NVFP4 f16 MFMA route)
   const int32_t* xexp;           // [m] their per-token exponents
@@ -95,6 +101,9 @@ hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
 // `marks` (nullable) receives an event record after each kernel: FC1, FC2, then the top-k
 // combine (the decode path records its last mark right after FC2).
 hipError_t launch_decode(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks);
+// True when the decode FC1 launch packs the routes itself for these sizes (the fused call then
+// launches no route pack); false for the grouped-GEMM path.
+bool decode_fc1_packs(const PreparedGeom& g, int64_t m, int topk);
 hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks);
 // out = bf16 of the sum of each token's valid route rows y[route] (route order).
 void launch_combine(const FusedParams& p, hipStream_t stream);

@@ -341,6 +341,32 @@ def test_fused_dropped_tokens_are_zero_and_m0(moe, device):
     assert out.shape == (0, cfg.hidden)
 
 
+@pytest.mark.parametrize("name,m", [("edge_s", 1), ("edge_s", 3), ("edge_s", 8), ("edge_s", 12), ("decode_s", 8)])
+def test_decode_path_map_and_dropped_routes(moe, device, name, m):
+    """The decode path with an expert map, -1 and out-of-range ids, an expert repeated inside one
+    token's top-k and a token whose routes are all dropped, run twice over the same workspace.
+    At these small shapes the FC1 launch packs the routes itself."""
+    cfg = SCALED[name]
+    case = make_case(cfg, m, seed=900 + m, weights="normal")
+    case.ids[0, 0] = -1
+    case.ids[0, 1] = cfg.num_global_experts + 3
+    if m > 1:
+        case.ids[1, 1] = case.ids[1, 0]
+        case.ids[m - 1, :] = -1
+    _say(f"decode path {name} m={m} map={case.emap is not None}: dropped and repeated routes")
+    layer = make_layer(case, device)
+    moe.moe_w4a16_set_path("decode")
+    try:
+        got = bf16_tensor_to_f64(run_layer(layer, case, device))
+        again = bf16_tensor_to_f64(run_layer(layer, case, device))
+    finally:
+        moe.moe_w4a16_set_path("auto")
+    if m > 1:
+        assert np.all(got[m - 1] == 0)
+    assert np.array_equal(got, again)
+    _check(case, got, label=f"decode path {name} m={m} dropped routes")
+
+
 # ----------------------------------------------------------------------------- full-size, sampled
 
 def _full_case(name, m, device, codes_dev=None):
@@ -351,10 +377,11 @@ def _full_case(name, m, device, codes_dev=None):
     return case
 
 
-@pytest.mark.parametrize("name,m", [("decode", 12), ("decode", 16), ("small", 16)])
+@pytest.mark.parametrize("name,m", [("decode", 12), ("decode", 16), ("small", 16), ("edge", 16)])
 def test_decode_path_full_size_above_eight_tokens(moe, device, name, m):
     """The decode path at 9..16 tokens stages more than 64 KiB of activation rows (one FC1
-    workgroup per CU): sampled full-size outputs against the oracle."""
+    workgroup per CU, routes packed by the route-pack launch; the edge shape adds an expert
+    map and -1 ids): sampled full-size outputs against the oracle."""
     cfg = C.get_config(name)
     case = _full_case(name, m, device)
     layer = make_layer(case, device, token_capacity=RP.token_capacity(m))
