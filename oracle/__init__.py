@@ -11,8 +11,9 @@ for the code formats, which the page names but does not define):
 
 * ``formats``    -- E2M1 / E4M3FN / E8M0 code tables, round-to-nearest-even
                     quantisers, MXFP4 (E8M0 per 32) and NVFP4 (E4M3 per 16 +
-                    fp32 global) quantise / dequantise, nibble packing, bf16
-                    rounding. Page: Description (NVFP4 weights; the new
+                    fp32 global) quantise / dequantise, MXFP8 (E4M3 per element,
+                    E8M0 per 32) for the W4A8 variant's FC2 operand, nibble
+                    packing, bf16 rounding. Page: Description (NVFP4 weights; the new
                     fp4_e8m0_k32 source with scale tails), Review round 1
                     (power-of-two-ceiling UE8M0 scale helper).
 * ``route_pack`` -- grouping of token x expert routes by expert into a padded,
@@ -24,7 +25,10 @@ for the code formats, which the page names but does not define):
 * ``moe``        -- FC1 -> SiLU-SwiGLU or relu2 -> FC2 and the router-weighted
                     top-k sum. Page: Description (fused FC1/FC2 kernel, top-k
                     sum folded into the FC2 store epilogue), Performance
-                    (relu2 and silu activations).
+                    (relu2 and silu activations); the W4A8 variant (review: the
+                    grouped MXFP8 quantisation of the SiLU-mul output, with an
+                    exact-silu reference) quantises the activation output to
+                    MXFP8 before FC2.
 
 Every function is pinned by tests under ``tests/`` against specification
 tables, closed forms, hand-computed cases, library decoders and brute force.

@@ -162,6 +162,45 @@ def quantise_mxfp4(w: np.ndarray):
     return pack_nibbles(codes), scales
 
 
+def quantise_mxfp8(a: np.ndarray):
+    """MXFP8 (E4M3 elements, one E8M0 scale per 32 along the last axis K).
+
+    The W4A8 variant quantises the activation output between FC1 and FC2 this way
+    (PR 4255 review: the grouped MXFP8 quantisation of the SiLU-mul output). Per
+    group (the last one holds K mod 32 elements when K is not a multiple of 32):
+    amax over the present elements; scale 2^ceil(log2(amax/448)) (the power-of-two
+    ceiling used for the MX weight scales), exponent clamped to [-127, 127], stored
+    as byte e+127; codes are E4M3 round-to-nearest-even of a / scale, so the largest
+    element lands in (224, 448] and nothing saturates. A group whose amax is 0
+    stores byte 0 and zero codes. Returns (codes uint8 [..., K], scales uint8
+    [..., ceil(K/32)]).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    k = a.shape[-1]
+    ng = -(-k // 32)
+    codes = np.zeros(a.shape, dtype=np.uint8)
+    scales = np.zeros(a.shape[:-1] + (ng,), dtype=np.uint8)
+    for gi in range(ng):
+        blk = a[..., gi * 32:(gi + 1) * 32]
+        amax = np.max(np.abs(blk), axis=-1)
+        nz = amax > 0
+        e = np.zeros(amax.shape, dtype=np.int64)
+        e[nz] = np.clip(ceil_log2(amax[nz] / E4M3_MAX), -127, 127)
+        scales[..., gi] = np.where(nz, e + 127, 0).astype(np.uint8)
+        q = e4m3_encode(blk * np.ldexp(1.0, -e)[..., None])
+        codes[..., gi * 32:(gi + 1) * 32] = np.where(nz[..., None], q, 0)
+    return codes, scales
+
+
+def dequant_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """a_hat[..., k] = e4m3(code) * 2^(scale[k // 32] - 127), float64."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    k = codes.shape[-1]
+    s = np.repeat(E8M0_TABLE[scales], 32, axis=-1)[..., :k]
+    return E4M3_TABLE[codes] * s
+
+
 def quantise_nvfp4(w: np.ndarray):
     """NVFP4 for [E, N, K] weights: E4M3 scale per 16 along K and one fp32 global scale per expert.
 

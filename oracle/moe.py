@@ -76,9 +76,19 @@ class Experts:
         return self._w2[e]
 
 
+def fc2_input(a: np.ndarray, mxfp8: bool) -> np.ndarray:
+    """The FC2 operand: the activation output itself (W4A16), or for the W4A8 variant its
+    MXFP8 quantisation along I, dequantised (the router weight is applied after FC2 either
+    way, so it is not quantised)."""
+    if not mxfp8:
+        return a
+    return formats.dequant_mxfp8(*formats.quantise_mxfp8(a))
+
+
 def moe_forward_loop(x: np.ndarray, topk_ids, topk_weights, expert_map, num_global_experts: int,
-                     num_experts: int, experts: Experts) -> np.ndarray:
-    """Route-by-route forward (the definition written out). x: float64 [m, H]."""
+                     num_experts: int, experts: Experts, mxfp8: bool = False) -> np.ndarray:
+    """Route-by-route forward (the definition written out). x: float64 [m, H].
+    ``mxfp8``: the W4A8 variant (the activation output quantised to MXFP8 before FC2)."""
     x = np.asarray(x, dtype=np.float64)
     m, k = np.asarray(topk_ids).shape
     lid = local_ids(topk_ids, expert_map, num_global_experts, num_experts).reshape(m, k)
@@ -90,13 +100,13 @@ def moe_forward_loop(x: np.ndarray, topk_ids, topk_weights, expert_map, num_glob
             if e < 0:
                 continue
             h = experts.w13(e) @ x[t]
-            a = activation(h, experts.act, experts.inter)
+            a = fc2_input(activation(h, experts.act, experts.inter), mxfp8)
             out[t] += w[t, j] * (experts.w2(e) @ a)
     return out
 
 
 def moe_forward(x: np.ndarray, topk_ids, topk_weights, expert_map, num_global_experts: int,
-                num_experts: int, experts: Experts, tokens=None, cols=None) -> np.ndarray:
+                num_experts: int, experts: Experts, tokens=None, cols=None, mxfp8: bool = False) -> np.ndarray:
     """Expert-grouped forward: the same per-route products, batched per expert with a matmul.
 
     ``tokens`` / ``cols`` restrict the result to a subset of tokens and output
@@ -114,7 +124,7 @@ def moe_forward(x: np.ndarray, topk_ids, topk_weights, expert_map, num_global_ex
     for e in np.unique(sub[sub >= 0]):
         tt, jj = np.nonzero(sub == e)                      # rows of `out`, route index
         h = x[tokens[tt]] @ experts.w13(int(e)).T          # [R, N1]
-        a = activation(h, experts.act, experts.inter)      # [R, I]
+        a = fc2_input(activation(h, experts.act, experts.inter), mxfp8)   # [R, I]
         y = a @ experts.w2(int(e))[cols].T                 # [R, len(cols)]
         np.add.at(out, tt, w[tokens[tt], jj][:, None] * y)
     return out
