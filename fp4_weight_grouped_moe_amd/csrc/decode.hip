@@ -378,14 +378,15 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
       }
       const int tok = info.x;
       if constexpr (F16) g13 = ldexpf(g13, tok >= 0 ? sp[tok] : 0);
-      const float rw = (tok >= 0) ? __int_as_float(info.y) * g2 : 0.f;
-      uint16_t* dst = p.inter + int64_t(blk * kBlockM + col) * g.ip;
+      // W4A8: the router weight and FC2 global scale come after FC2 (outside the quantisation)
+      const float rw = (tok >= 0) ? (p.w4a8 ? 1.f : __int_as_float(info.y) * g2) : 0.f;
+      const int64_t slot = int64_t(blk) * kBlockM + col;
       const int r0 = 4 * q;
       if (g.act == ACT_SWIGLU) {
         float a[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[i] = silu_f32(h0[i] * g13) * (h1[i] * g13) * rw;
-        *reinterpret_cast<uint2*>(dst + it * 16 + r0) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+        store_inter4(p, slot, it * 16 + r0, a);
       } else {
         float a[4], b[4];
 #pragma unroll
@@ -394,8 +395,8 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
           a[i] = x0 * x0 * rw;
           b[i] = x1 * x1 * rw;
         }
-        *reinterpret_cast<uint2*>(dst + 32 * it + r0) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
-        *reinterpret_cast<uint2*>(dst + 32 * it + 16 + r0) = make_uint2(pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3]));
+        store_inter4(p, slot, 32 * it + r0, a);
+        store_inter4(p, slot, 32 * it + 16 + r0, b);
       }
     }
     acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -498,8 +499,9 @@ __global__ __launch_bounds__(kF2Threads, 1) void decode_fc2_kernel(FusedParams p
     }
     const int tok = stok[blk * kBlockM + col];
     if (tok >= 0) {
+      const float wt = p.w4a8 ? __int_as_float(p.slot_info[blk * kBlockM + col].y) * scalar_load(p.g2, uniform(be[blk])) : 1.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) atomicAdd(&tacc[wave][tok][4 * q + i], acc[i]);
+      for (int i = 0; i < 4; ++i) atomicAdd(&tacc[wave][tok][4 * q + i], acc[i] * wt);
     }
   };
 
@@ -589,6 +591,8 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
   // Staging: the slot -> route table and each route's K slice by DMA (dropped routes, the
   // table's tail and K blocks past kb2 read as zeros).
   for (int i = tid; i < kF3Waves * m * 16 * RG; i += kF3Threads) tacc[i] = 0.f;
+  if (!(FMT == FMT_NVFP4) && p.w4a8)
+    for (int r = tid; r < routes; r += kF3Threads) sexp[r] = __float_as_int(p.topk_weights[r]);
   const __amdgpu_buffer_rsrc_t tr = buffer_rsrc(p.sorted_route_ids, uint32_t(nb * kBlockM * 4));
   for (int n = wave; n * 64 < nb * kBlockM; n += kF3Waves) dma4(tr, sroute + 64 * n, uint32_t((64 * n + lane) * 4));
   // The route -> slot lookups of all of a wave's rows go out together, then the row DMAs.
@@ -701,10 +705,12 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
     if (route >= 0) {
       float* ta = tacc + (wave * m + route / topk) * (16 * RG) + 4 * q;
       const int pe = F16 ? sexp[route] : 0;
+      // W4A8 (MXFP4 only, so the exponent area is free): router weight x FC2 global scale
+      const float wt = !F16 && p.w4a8 ? __int_as_float(sexp[route]) * scalar_load(p.g2, scalar_load(p.block_expert, blk)) : 1.f;
 #pragma unroll
       for (int rr = 0; rr < RG; ++rr)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) atomicAdd(ta + 16 * rr + i, F16 ? ldexpf(acc[rr][i], pe) : acc[rr][i]);
+        for (int i = 0; i < 4; ++i) atomicAdd(ta + 16 * rr + i, F16 ? ldexpf(acc[rr][i], pe) : acc[rr][i] * wt);
     }
   };
 
@@ -787,6 +793,8 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
   else
     hipLaunchKernelGGL((decode_fc1_kernel<FMT, false, false>), dim3(grid1), dim3(kF1Threads), 0, stream, p);
   if (marks) (void)hipEventRecord(marks[0], stream);
+  if (p.w4a8)
+    if (hipError_t e = launch_mxfp8_requant(p, stream); e != hipSuccess) return e;
   constexpr int RG = kF3RowGroups;
   const size_t lds3 = f3_lds_bytes<RG>(p.m, p.topk, p.cap_blocks);
   // (the intermediate rows are addressed through a buffer resource: 32-bit offsets)

@@ -174,6 +174,18 @@ __device__ __forceinline__ float scalar_load(const float* p, int i) {
   return ((const __attribute__((address_space(4))) float*)p)[i];
 }
 
+// FC1's activation output: four consecutive intermediate columns of one slot row, in bf16
+// (W4A16), or in fp32 for the W4A8 variant's MXFP8 rounding pass (rounding to bf16 first
+// would round twice: a bf16 value lies on an E4M3 midpoint once in 16). P: the fused-layer
+// parameter block.
+template <typename P>
+__device__ __forceinline__ void store_inter4(const P& p, int64_t slot, int64_t col, const float* v) {
+  if (p.w4a8)
+    *reinterpret_cast<f32x4*>(p.inter32 + slot * p.g.ip + col) = f32x4{v[0], v[1], v[2], v[3]};
+  else
+    *reinterpret_cast<uint2*>(p.inter + slot * p.g.ip + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();

@@ -280,9 +280,9 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
         const int64_t slot = (fb + b) * kBlockM + col;
         const int2 info = p.slot_info[slot];
         const bool valid = info.x >= 0;
-        const float rw = valid ? __int_as_float(info.y) * g2 : 0.f;
+        // W4A8: the router weight and FC2 global scale come after FC2 (outside the quantisation)
+        const float rw = valid ? (p.w4a8 ? 1.f : __int_as_float(info.y) * g2) : 0.f;
         const float s13 = F16 && valid ? ldexpf(g13, p.xexp[info.x]) : g13;
-        uint16_t* dst = p.inter + slot * g.ip;
         if (g.act == ACT_SWIGLU) {
 #pragma unroll
           for (int pr = 0; pr < FR / 2; ++pr) {
@@ -292,7 +292,7 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
               for (int i = 0; i < 4; ++i)
                 v[i] = silu_f32(acc[2 * pr][bb][i] * s13) * (acc[2 * pr + 1][bb][i] * s13) * rw;
               const int64_t icol = int64_t((rg_base + 2 * pr) >> 1) * 16 + r0;
-              *reinterpret_cast<uint2*>(dst + icol) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+              store_inter4(p, slot, icol, v);
             }
           }
         } else {
@@ -306,7 +306,7 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
                 v[i] = u * u * rw;
               }
               const int64_t icol = int64_t(rg_base + f) * 16 + r0;
-              *reinterpret_cast<uint2*>(dst + icol) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+              store_inter4(p, slot, icol, v);
             }
           }
         }
@@ -319,10 +319,11 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
       if (b < nb) {
         const int r = p.sorted_route_ids[(fb + b) * kBlockM + col];
         if (r >= 0) {
+          const float wt = p.w4a8 ? __int_as_float(p.slot_info[(fb + b) * kBlockM + col].y) * p.g2[e] : 1.f;
 #pragma unroll
           for (int f = 0; f < FR; ++f) {
             const int64_t h = int64_t(rg_base + f) * 16 + r0;
-            if (h < g.H) *reinterpret_cast<f32x4*>(p.y + int64_t(r) * g.H + h) = acc[f][bb];
+            if (h < g.H) *reinterpret_cast<f32x4*>(p.y + int64_t(r) * g.H + h) = acc[f][bb] * wt;
           }
         }
       }
@@ -443,6 +444,8 @@ hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hi
   if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 1>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 1>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   if (marks) (void)hipEventRecord(marks[0], stream);
+  if (p.w4a8)
+    if (hipError_t e2 = launch_mxfp8_requant(p, stream); e2 != hipSuccess) return e2;
   if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   if (marks) (void)hipEventRecord(marks[1], stream);

@@ -70,6 +70,11 @@ struct FusedParams {
   const float* topk_weights;     // [m * topk]
   const int32_t* expert_map;     // [num_global_experts] or null
   int32_t num_global_experts;
+  // W4A8 variant: FC1 stores the activation output without the router weight, the output
+  // rows are rounded to MXFP8 in place (launch_mxfp8_requant), and FC2 applies router weight x
+  // FC2 global scale per route.
+  int32_t w4a8;
+  float* inter32;                // W4A8: fp32 [cap_routes, ip] activation output of FC1
   uint16_t* inter;               // bf16 [cap_routes, ip]
   const uint16_t* x16;           // f16 [m, H] scaled activations (NVFP4 f16 MFMA route)
   const int32_t* xexp;           // [m] their per-token exponents
@@ -107,5 +112,7 @@ bool decode_fc1_packs(const PreparedGeom& g, int64_t m, int topk);
 hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks);
 // out = bf16 of the sum of each token's valid route rows y[route] (route order).
 void launch_combine(const FusedParams& p, hipStream_t stream);
+// W4A8: every valid intermediate row rounded to MXFP8 in place (between FC1 and FC2).
+hipError_t launch_mxfp8_requant(const FusedParams& p, hipStream_t stream);
 
 }  // namespace moe

@@ -112,7 +112,7 @@ inline bool decode_stages_x(const PreparedGeom& g, int64_t m) { return m * decod
 // decode path the fp32 FC2 partial sums of each K split with their arrival counts.
 struct FusedGeom {
   PackGeom pack;
-  size_t off_pack, off_inter, off_x16, off_xexp, off_y, off_part, off_count, total;
+  size_t off_pack, off_inter, off_inter32, off_x16, off_xexp, off_y, off_part, off_count, total;
 };
 
 __host__ __device__ inline FusedGeom make_fused_geom(const PreparedGeom& w, int64_t cap, int64_t k) {
@@ -121,6 +121,8 @@ __host__ __device__ inline FusedGeom make_fused_geom(const PreparedGeom& w, int6
   size_t o = 0;
   f.off_pack = o;  o = align256(o + f.pack.total);
   f.off_inter = o; o = align256(o + size_t(f.pack.cap_routes) * w.ip * 2);
+  // W4A8 (MXFP4 weights): the fp32 activation output, rounded to MXFP8 into the bf16 rows above
+  f.off_inter32 = o; o = align256(o + (w.fmt == FMT_MXFP4 ? size_t(f.pack.cap_routes) * w.ip * 4 : 0));
   f.off_x16 = o;   o = align256(o + size_t(cap) * w.H * 2);
   f.off_xexp = o;  o = align256(o + size_t(cap) * 4);
   f.off_y = o;     o = align256(o + size_t(cap) * k * w.H * 4);

@@ -190,6 +190,22 @@ int moe_w4a16_fused(const moe_w4a16_dims* dims, const void* prepared, size_t pre
                     int num_global_experts, int64_t token_capacity, void* workspace,
                     size_t workspace_bytes, uint16_t* out, hipStream_t stream);
 
+/* W4A8 variant of the same layer. Page: PR 4255 review (a grouped MXFP8 quantisation of the
+ * SiLU-mul output, checked against a Torch reference with the exact silu). The activation
+ * output of every route is rounded to MXFP8 before FC2 -- E4M3FN elements, one E8M0 scale per
+ * 32 along the intermediate axis, scale 2^ceil(log2(amax / 448)), ties to even -- and the
+ * router weight is applied after FC2, outside the quantisation; FC1 is the W4A16 one.
+ * out[t] = sum_j w[t, j] * W2_e @ MXFP8(act(W13_e @ x_t)) over surviving routes.
+ * Arguments, layouts, ownership and errors as moe_w4a16_fused (same prepared buffer and
+ * workspace); MOE_ERR_UNSUPPORTED unless dims->fmt is MOE_FMT_MXFP4_E8M0_K32 (the gfx950
+ * block-scaled MFMA applies E8M0 scales only). The GPU rounds the bf16 activation output
+ * (the W4A16 intermediate) and FC2 multiplies the exact MXFP8 values on the bf16 MFMA. */
+int moe_w4a8_fused(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes,
+                   const uint16_t* x, int64_t m, const int32_t* topk_ids,
+                   const float* topk_weights, int topk, const int32_t* expert_map,
+                   int num_global_experts, int64_t token_capacity, void* workspace,
+                   size_t workspace_bytes, uint16_t* out, hipStream_t stream);
+
 /* ------------------------------------------------------------------ diagnostics */
 
 /* Measurement twin of moe_w4a16_fused: the same launches on `stream`, with HIP event

@@ -70,7 +70,7 @@ def experts_for(case: Case, experts=None) -> M.Experts:
     return M.Experts(cfg.fmt, cfg.act, cfg.hidden, cfg.inter, sub, expert_ids=ids)
 
 
-def oracle_out(case: Case, tokens=None, cols=None) -> np.ndarray:
+def oracle_out(case: Case, tokens=None, cols=None, mxfp8: bool = False) -> np.ndarray:
     from oracle.route_pack import local_ids
 
     cfg = case.cfg
@@ -82,7 +82,7 @@ def oracle_out(case: Case, tokens=None, cols=None) -> np.ndarray:
         needed = np.unique(lid[t][lid[t] >= 0])
     ex = experts_for(case, needed)
     return M.moe_forward(x, case.ids, case.w, case.emap, cfg.num_global_experts, cfg.num_experts, ex,
-                         tokens=tokens, cols=cols)
+                         tokens=tokens, cols=cols, mxfp8=mxfp8)
 
 
 def bf16_tensor_to_f64(t) -> np.ndarray:
@@ -111,12 +111,12 @@ def make_layer(case: Case, device, token_capacity: Optional[int] = None):
     return layer
 
 
-def run_layer(layer, case: Case, device, out=None):
+def run_layer(layer, case: Case, device, out=None, w4a8=False):
     import torch
 
     x = dev(case.xbits.view(np.int16), device).view(torch.bfloat16)
     emap = dev(case.emap, device) if case.emap is not None else None
     out = layer(x, dev(case.ids, device), dev(case.w, device), expert_map=emap,
-                num_global_experts=case.cfg.num_global_experts, out=out)
+                num_global_experts=case.cfg.num_global_experts, out=out, w4a8=w4a8)
     torch.cuda.synchronize()
     return out
