@@ -39,12 +39,15 @@ def moe():
     m.moe_w4a16_set_path("auto")
 
 
-@pytest.mark.parametrize("name,m,path", [("decode_s", 8, "decode"), ("small_s", 16, "decode"),
-                                         ("edge_s", 100, "gemm"), ("prefill_s", 300, "gemm")])
-def test_graph_replay_matches_eager(moe, device, name, m, path):
+@pytest.mark.parametrize("name,m,path,w4a8", [("decode_s", 8, "decode", False), ("small_s", 16, "decode", False),
+                                              ("edge_s", 100, "gemm", False), ("prefill_s", 300, "gemm", False),
+                                              ("edge_s", 8, "decode", True), ("edge_s", 100, "gemm", True)])
+def test_graph_replay_matches_eager(moe, device, name, m, path, w4a8):
+    """w4a8: the W4A8 entry point (moe_w4a8_fused), whose MXFP8 rounding pass is one more launch
+    in the captured graph."""
     import torch
 
-    print(f"graph {name} m={m} path={path}", flush=True)
+    print(f"graph {name} m={m} path={path} w4a8={w4a8}", flush=True)
     cfg = SCALED[name]
     case0 = make_case(cfg, m, seed=cfg.index * 7 + m + 3, weights="normal")
     cases = [case0]
@@ -69,7 +72,7 @@ def test_graph_replay_matches_eager(moe, device, name, m, path):
             emap.copy_(torch.from_numpy(c.emap))
 
     def call():
-        layer(x, ids, wts, expert_map=emap, num_global_experts=cfg.num_global_experts, out=out)
+        layer(x, ids, wts, expert_map=emap, num_global_experts=cfg.num_global_experts, out=out, w4a8=w4a8)
 
     moe.moe_w4a16_set_path(path)
     try:
@@ -103,7 +106,7 @@ def test_graph_replay_matches_eager(moe, device, name, m, path):
             # eager work on the same stream between replays
             assert float((x.float() * 0.5).sum().item()) == pytest.approx(float(x.float().sum().item()) * 0.5, rel=1e-3)
 
-        ok, err, bound = M.within_tolerance(bf16_tensor_to_f64(out), oracle_out(cases[(6 - 1) % len(cases)]))
+        ok, err, bound = M.within_tolerance(bf16_tensor_to_f64(out), oracle_out(cases[(6 - 1) % len(cases)], mxfp8=w4a8))
         assert ok, f"{name}: {err} > {bound}"
         del graph
     finally:
