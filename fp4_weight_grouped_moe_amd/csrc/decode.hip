@@ -561,7 +561,21 @@ __host__ __device__ inline size_t f3_lds_bytes(int64_t m, int64_t topk, int64_t 
   return f3_rows_bytes(m * topk) + f3_table_bytes(cap_blocks) + f3_exp_bytes(m * topk) + size_t(kF3Waves) * m * 16 * RG * 4;
 }
 
-template <int FMT, int RG>
+// W8 (W4A8, block-scaled MFMA): each route's K slice as MXFP8 codes (256 B) and its 8 E8M0
+// bytes, plus a 1 KiB fragment-transposition area per wave.
+constexpr int kF8RowBytes = kF3KB * kKBlock;
+__host__ __device__ inline size_t f8_rows_bytes(int64_t routes) { return (size_t(routes) * kF8RowBytes + 1023) / 1024 * 1024; }
+__host__ __device__ inline size_t f8_scale_bytes(int64_t routes) { return (size_t(routes) * 8 + 15) / 16 * 16; }
+constexpr size_t kF8Transpose = size_t(kF3Waves) * 1024;
+template <int RG>
+__host__ __device__ inline size_t f8_lds_bytes(int64_t m, int64_t topk, int64_t cap_blocks) {
+  return f8_rows_bytes(m * topk) + f8_scale_bytes(m * topk) + kF8Transpose + f3_table_bytes(cap_blocks) +
+         f3_exp_bytes(m * topk) + size_t(kF3Waves) * m * 16 * RG * 4;
+}
+
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+template <int FMT, int RG, bool W8>
 __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedParams p) {
   extern __shared__ __align__(16) uint8_t dyn[];
   const PreparedGeom& g = p.g;
@@ -580,8 +594,12 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
   const int z = 2 * (pair % npair) + ((int(blockIdx.x) >> 3) & 1), G = pair / npair;
   if (G >= ngroup || z >= nsplit) return;
   const int kq0 = z * kF3KB;
-  uint8_t* bs = dyn;                                                        // [routes][kF3RowBytes]
-  int* sroute = reinterpret_cast<int*>(dyn + f3_rows_bytes(routes));       // [nb * 16] slot -> route
+  uint8_t* bs = dyn;                                                        // [routes][kF3RowBytes] (W8: kF8RowBytes)
+  // W8: E8M0 bytes [routes][8] and the per-wave transposition areas after the rows
+  uint32_t* ssc = reinterpret_cast<uint32_t*>(dyn + f8_rows_bytes(routes));
+  uint32_t* xtr = reinterpret_cast<uint32_t*>(dyn + f8_rows_bytes(routes) + f8_scale_bytes(routes)) + wave * 256;
+  int* sroute = reinterpret_cast<int*>(dyn + (W8 ? f8_rows_bytes(routes) + f8_scale_bytes(routes) + kF8Transpose
+                                                  : f3_rows_bytes(routes)));   // [nb * 16] slot -> route
   int* sexp = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(sroute) + f3_table_bytes(p.cap_blocks));    // [routes] f16 exponents
   float* tacc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sexp) + f3_exp_bytes(routes));          // [waves][m][16 RG]
   const int U = nb > wave ? (nb - wave + kF3Waves - 1) / kF3Waves : 0;
@@ -596,19 +614,30 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
   const __amdgpu_buffer_rsrc_t tr = buffer_rsrc(p.sorted_route_ids, uint32_t(nb * kBlockM * 4));
   for (int n = wave; n * 64 < nb * kBlockM; n += kF3Waves) dma4(tr, sroute + 64 * n, uint32_t((64 * n + lane) * 4));
   // The route -> slot lookups of all of a wave's rows go out together, then the row DMAs.
-  const __amdgpu_buffer_rsrc_t ir = buffer_rsrc(p.inter, uint32_t(p.cap_blocks * kBlockM * g.ip * 2));
-  const int nchunk = int(f3_rows_bytes(routes) / 1024);
+  constexpr int kRowB = W8 ? kF8RowBytes : kF3RowBytes;     // staged bytes per route
+  constexpr int kElB = W8 ? 1 : 2;                           // bytes per element
+  const __amdgpu_buffer_rsrc_t ir = W8 ? buffer_rsrc(p.inter8, uint32_t(p.cap_blocks * kBlockM * g.ip))
+                                       : buffer_rsrc(p.inter, uint32_t(p.cap_blocks * kBlockM * g.ip * 2));
+  const int nchunk = int((W8 ? f8_rows_bytes(routes) : f3_rows_bytes(routes)) / 1024);
   int slot[kF3MaxRowDma];
 #pragma unroll
   for (int i = 0; i < kF3MaxRowDma; ++i) {
-    const int n = wave + kF3Waves * i, r = (n * 1024 + lane * 16) / kF3RowBytes;
+    const int n = wave + kF3Waves * i, r = (n * 1024 + lane * 16) / kRowB;
     slot[i] = n < nchunk && r < routes ? p.route_slot[r] : -1;
   }
 #pragma unroll
   for (int i = 0; i < kF3MaxRowDma; ++i) {
-    const int n = wave + kF3Waves * i, o = (n * 1024 + lane * 16) % kF3RowBytes;
-    const bool ok = slot[i] >= 0 && kq0 + o / (kKBlock * 2) < kb2;
-    if (n < nchunk) dma16(ir, bs + n * 1024, ok ? uint32_t(slot[i] * g.ip * 2 + kq0 * kKBlock * 2 + o) : kOutOfRange);
+    const int n = wave + kF3Waves * i, o = (n * 1024 + lane * 16) % kRowB;
+    const bool ok = slot[i] >= 0 && kq0 + o / (kKBlock * kElB) < kb2;
+    if (n < nchunk) dma16(ir, bs + n * 1024, ok ? uint32_t((slot[i] * g.ip + kq0 * kKBlock) * kElB + o) : kOutOfRange);
+  }
+  if constexpr (W8) {
+    // each route's two scale dwords (K blocks kq0, kq0 + 1; 2^0 where there is no route or block)
+    for (int i = tid; i < 2 * routes; i += kF3Threads) {
+      const int r = i >> 1, h = i & 1, sl = p.route_slot[r];
+      ssc[i] = sl >= 0 && kq0 + h < kb2 ? *reinterpret_cast<const uint32_t*>(p.sc8 + int64_t(sl) * (g.ip / 32) + (kq0 + h) * 4)
+                                        : 0x7F7F7F7Fu;
+    }
   }
 
   // Loads are unconditional so that the wait counters stay exact: units past the end re-read
@@ -678,10 +707,36 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
     if (u >= U) return;
     const int blk = wave + u * kF3Waves;
     const int route = sroute[blk * kBlockM + col];
-    const uint8_t* brow = bs + max(route, 0) * kF3RowBytes + q * 16;
+    const uint8_t* brow = bs + max(route, 0) * kRowB + q * 16;
     f32x4 acc[RG];
 #pragma unroll
     for (int rr = 0; rr < RG; ++rr) acc[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (W8) {
+      // Block-scaled FP4 x FP8 MFMA, one per (row group, K block). B (the routes' MXFP8 row):
+      // lane (col, q) holds K 16 q .. 16 q + 15 and 64 + 16 q .. 64 + 16 q + 15 of route col; its
+      // scale byte is block q of that route. A (the weights): lane (col, q) must hold the 32
+      // consecutive K of block q of row col, while the fragment layout deals them out in
+      // 8-K chunks over the four lane quarters (chunk 4 s + q in dword s): a 4 x 4 transpose
+      // through this wave's LDS area (LDS operations of one wave complete in order).
+#pragma unroll
+      for (int j = 0; j < kF3KB; ++j) {
+        if (kq0 + j < kb2) {
+          const u32x4 blo = route >= 0 ? *reinterpret_cast<const u32x4*>(brow + j * kKBlock) : u32x4{0u, 0u, 0u, 0u};
+          const u32x4 bhi = route >= 0 ? *reinterpret_cast<const u32x4*>(brow + j * kKBlock + 64) : u32x4{0u, 0u, 0u, 0u};
+          const i32x8 bop = i32x8{int(blo[0]), int(blo[1]), int(blo[2]), int(blo[3]), int(bhi[0]), int(bhi[1]), int(bhi[2]), int(bhi[3])};
+          const int sb = route >= 0 ? int((ssc[route * 2 + j] >> (8 * q)) & 0xFFu) : 127;
+#pragma unroll
+          for (int rr = 0; rr < RG; ++rr) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) xtr[col * 16 + 4 * s + q] = r.q[rr][j][s];
+            const u32x4 a = *reinterpret_cast<const u32x4*>(xtr + col * 16 + 4 * q);
+            const i32x8 aop = i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
+            const int sa = int((r.s[rr][j] >> (8 * q)) & 0xFFu);
+            acc[rr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[rr], 4, 0, 0, sa, 0, sb);
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < kF3KB; ++j) {
       if (kq0 + j < kb2) {
@@ -701,6 +756,7 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
           }
         }
       }
+    }
     }
     if (route >= 0) {
       float* ta = tacc + (wave * m + route / topk) * (16 * RG) + 4 * q;
@@ -774,7 +830,8 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
     hipError_t e = allow_lds(&decode_fc1_kernel<FMT, true, false>, kDecodeStageBytes + 256);
     if (e == hipSuccess) e = allow_lds(&decode_fc1_kernel<FMT, true, true>, kLdsPerCU - kF1StaticLds);
     if (e == hipSuccess) e = allow_lds(&decode_fc2_kernel<FMT>, 98304);
-    if (e == hipSuccess) e = allow_lds(&decode_fc2_split_kernel<FMT, kF3RowGroups>, kF3MaxLds);
+    if (e == hipSuccess) e = allow_lds(&decode_fc2_split_kernel<FMT, kF3RowGroups, false>, kF3MaxLds);
+    if (FMT == FMT_MXFP4 && e == hipSuccess) e = allow_lds(&decode_fc2_split_kernel<FMT_MXFP4, kF3RowGroups, true>, kF3MaxLds);
     return e;
   }();
   if (lds_ok != hipSuccess) return lds_ok;
@@ -793,16 +850,25 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
   else
     hipLaunchKernelGGL((decode_fc1_kernel<FMT, false, false>), dim3(grid1), dim3(kF1Threads), 0, stream, p);
   if (marks) (void)hipEventRecord(marks[0], stream);
-  if (p.w4a8)
-    if (hipError_t e = launch_mxfp8_requant(p, stream); e != hipSuccess) return e;
   constexpr int RG = kF3RowGroups;
   const size_t lds3 = f3_lds_bytes<RG>(p.m, p.topk, p.cap_blocks);
   // (the intermediate rows are addressed through a buffer resource: 32-bit offsets)
-  if (lds3 <= size_t(kF3MaxLds) && f3_rows_bytes(p.m * p.topk) <= size_t(kF3MaxRowDma) * kF3Waves * 1024 &&
-      p.cap_blocks * kBlockM * g.ip * 2 <= int64_t(INT32_MAX)) {
+  const bool split = lds3 <= size_t(kF3MaxLds) && f3_rows_bytes(p.m * p.topk) <= size_t(kF3MaxRowDma) * kF3Waves * 1024 &&
+                     p.cap_blocks * kBlockM * g.ip * 2 <= int64_t(INT32_MAX);
+  // W4A8: the K-split FC2 runs the block-scaled FP4 x FP8 MFMA on the MXFP8 codes; otherwise
+  // FC2 multiplies their exact values in bf16
+  const bool w8 = FMT == FMT_MXFP4 && p.w4a8 && p.inter8 != nullptr && split &&
+                  f8_lds_bytes<RG>(p.m, p.topk, p.cap_blocks) <= size_t(kF3MaxLds);
+  if (p.w4a8)
+    if (hipError_t e = launch_mxfp8_requant(p, w8, stream); e != hipSuccess) return e;
+  if (split) {
     const int nsplit = int((g.kb2 + kF3KB - 1) / kF3KB);
     const int64_t pairs = ((g.n2_groups + RG - 1) / RG) * ((nsplit + 1) / 2);
-    hipLaunchKernelGGL((decode_fc2_split_kernel<FMT, RG>), dim3((pairs + 7) / 8 * 16), dim3(kF3Threads), lds3, stream, p);
+    if (w8)
+      hipLaunchKernelGGL((decode_fc2_split_kernel<FMT_MXFP4, RG, true>), dim3((pairs + 7) / 8 * 16), dim3(kF3Threads),
+                         f8_lds_bytes<RG>(p.m, p.topk, p.cap_blocks), stream, p);
+    else
+      hipLaunchKernelGGL((decode_fc2_split_kernel<FMT, RG, false>), dim3((pairs + 7) / 8 * 16), dim3(kF3Threads), lds3, stream, p);
     if (marks) {
       (void)hipEventRecord(marks[1], stream);
       (void)hipEventRecord(marks[2], stream);

@@ -445,7 +445,7 @@ hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hi
   else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 1>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   if (marks) (void)hipEventRecord(marks[0], stream);
   if (p.w4a8)
-    if (hipError_t e2 = launch_mxfp8_requant(p, stream); e2 != hipSuccess) return e2;
+    if (hipError_t e2 = launch_mxfp8_requant(p, false, stream); e2 != hipSuccess) return e2;
   if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   if (marks) (void)hipEventRecord(marks[1], stream);

@@ -75,6 +75,8 @@ struct FusedParams {
   // FC2 global scale per route.
   int32_t w4a8;
   float* inter32;                // W4A8: fp32 [cap_routes, ip] activation output of FC1
+  uint8_t* inter8;               // W4A8, decode path: MXFP8 codes [cap_routes, ip] (E4M3)
+  uint8_t* sc8;                  //   and their E8M0 scales [cap_routes, ip / 32]
   uint16_t* inter;               // bf16 [cap_routes, ip]
   const uint16_t* x16;           // f16 [m, H] scaled activations (NVFP4 f16 MFMA route)
   const int32_t* xexp;           // [m] their per-token exponents
@@ -112,7 +114,8 @@ bool decode_fc1_packs(const PreparedGeom& g, int64_t m, int topk);
 hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks);
 // out = bf16 of the sum of each token's valid route rows y[route] (route order).
 void launch_combine(const FusedParams& p, hipStream_t stream);
-// W4A8: every valid intermediate row rounded to MXFP8 in place (between FC1 and FC2).
-hipError_t launch_mxfp8_requant(const FusedParams& p, hipStream_t stream);
+// W4A8: every valid intermediate row rounded to MXFP8 (between FC1 and FC2): as the exact
+// values in the bf16 rows, or (codes = true) as E4M3 codes and E8M0 scale bytes.
+hipError_t launch_mxfp8_requant(const FusedParams& p, bool codes, hipStream_t stream);
 
 }  // namespace moe

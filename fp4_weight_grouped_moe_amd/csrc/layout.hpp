@@ -112,7 +112,7 @@ inline bool decode_stages_x(const PreparedGeom& g, int64_t m) { return m * decod
 // decode path the fp32 FC2 partial sums of each K split with their arrival counts.
 struct FusedGeom {
   PackGeom pack;
-  size_t off_pack, off_inter, off_inter32, off_x16, off_xexp, off_y, off_part, off_count, total;
+  size_t off_pack, off_inter, off_inter32, off_inter8, off_sc8, off_x16, off_xexp, off_y, off_part, off_count, total;
 };
 
 __host__ __device__ inline FusedGeom make_fused_geom(const PreparedGeom& w, int64_t cap, int64_t k) {
@@ -123,6 +123,10 @@ __host__ __device__ inline FusedGeom make_fused_geom(const PreparedGeom& w, int6
   f.off_inter = o; o = align256(o + size_t(f.pack.cap_routes) * w.ip * 2);
   // W4A8 (MXFP4 weights): the fp32 activation output, rounded to MXFP8 into the bf16 rows above
   f.off_inter32 = o; o = align256(o + (w.fmt == FMT_MXFP4 ? size_t(f.pack.cap_routes) * w.ip * 4 : 0));
+  // W4A8 on the decode path: the MXFP8 codes and E8M0 scale bytes themselves (block-scaled FC2)
+  const bool w8 = w.fmt == FMT_MXFP4 && cap <= kDecodeMaxM;
+  f.off_inter8 = o; o = align256(o + (w8 ? size_t(f.pack.cap_routes) * w.ip : 0));
+  f.off_sc8 = o;    o = align256(o + (w8 ? size_t(f.pack.cap_routes) * (w.ip / 32) : 0));
   f.off_x16 = o;   o = align256(o + size_t(cap) * w.H * 2);
   f.off_xexp = o;  o = align256(o + size_t(cap) * 4);
   f.off_y = o;     o = align256(o + size_t(cap) * k * w.H * 4);
