@@ -113,18 +113,20 @@ def test_w4a8_matches_oracle_scaled(moe, device, name, m, path):
     _check(case, got8, label=f"w4a8 {name} m={m} {path}")
 
 
-def test_w4a8_full_size_edge_sampled(moe, device):
+@pytest.mark.parametrize("m", [512, 16, 8])
+def test_w4a8_full_size_edge_sampled(moe, device, m):
+    """Full-size edge shape: m = 512 on the grouped GEMM (FC2 on the exact MXFP8 values in bf16);
+    m = 16 and 8 on the decode path (FC2 on the block-scaled FP4 x FP8 MFMA)."""
     cfg = C.get_config("edge")
-    m = 512
     case = make_case(cfg, m, seed=cfg.index * 1000 + m, weights="none")
     case.codes_dev = D.draw_random_codes_torch(cfg, seed=1000 + cfg.index, device=device)
     layer = make_layer(case, device, token_capacity=RP.token_capacity(m))
-    _say("w4a8 full edge m=512")
+    _say(f"w4a8 full edge m={m}")
     got = bf16_tensor_to_f64(run_layer(layer, case, device, w4a8=True))
     rng = np.random.default_rng(21)
     tokens = np.unique(np.array([0, m - 1, rng.integers(0, m)]))
     cols = np.sort(rng.choice(cfg.hidden, size=96, replace=False))
-    _check(case, got, tokens=tokens, cols=cols, label="w4a8 edge m=512")
+    _check(case, got, tokens=tokens, cols=cols, label=f"w4a8 edge m={m}")
     assert np.all(np.isfinite(got))
     del layer, case
     torch.cuda.empty_cache()
