@@ -7,6 +7,8 @@
 // needed.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "device.hpp"
 #include "kernels.hpp"
 #include "layout.hpp"
@@ -45,6 +47,11 @@ constexpr int kLoadBatch = 8;
 __host__ __device__ inline bool segmented_pack(int64_t num_routes, int num_experts) {
   return num_routes > kPackThreads && num_routes <= kCacheRoutes && num_experts <= kSegExperts;
 }
+// Up to this many experts the segmented pack ranks each 64-route chunk with per-wave 64-bit
+// lane masks per expert in LDS (one atomic OR and one read per lane) instead of one ballot
+// pass per distinct expert (30 of the 46 us of a 16 384-route, 256-expert pack).
+constexpr int kMaskExperts = 256;
+__host__ __device__ inline bool mask_ranks(int num_experts) { return num_experts <= kMaskExperts; }
 
 __device__ void cache_routes(const RoutePackParams& p, int16_t* lc, int* cnt) {
   const int tid = threadIdx.x;
@@ -145,6 +152,8 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   int16_t* lc = reinterpret_cast<int16_t*>(smem + route_pack_base_lds(E));                          // [R] local ids
   uint16_t* srank = reinterpret_cast<uint16_t*>(smem + route_pack_base_lds(E) + size_t(kCacheRoutes) * 2);   // [R] rank in segment
   uint16_t* scnt = srank + kCacheRoutes;                                                            // [waves][E] counts, then bases
+  uint64_t* wmask = reinterpret_cast<uint64_t*>(smem + route_pack_base_lds(E) + size_t(kCacheRoutes) * 4 +
+                                                (size_t(kPackWaves) * E * 2 + 7) / 8 * 8);          // [waves][E] lane masks
 
   // Small batches (one chunk) keep the first chunk's local id and router weight in
   // registers; larger ones up to kCacheRoutes keep every route's in LDS. Either way
@@ -156,6 +165,8 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   for (int i = tid; i < kPackWaves * E; i += kPackThreads) wcnt[i] = 0;
   if (cached)
     for (int i = tid; i < kPackWaves * E; i += kPackThreads) scnt[i] = 0;
+  if (cached && mask_ranks(E))
+    for (int i = tid; i < kPackWaves * E; i += kPackThreads) wmask[i] = 0;
   __syncthreads();
   if (cached) {
     cache_routes(p, lc, cnt);
@@ -249,14 +260,26 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
       int rank = 0, same = 0;
       uint64_t todo = __ballot(l >= 0);
       valid_total += __popcll(todo);
-      while (todo) {
-        const int v = __builtin_amdgcn_readlane(l, __builtin_ctzll(todo));
-        const uint64_t mv = __ballot(l == v);
-        if (l == v) {
-          rank = __popcll(mv & lt_mask);
-          same = __popcll(mv);
+      if (mask_ranks(E)) {
+        // The lanes of expert v set their bits in this wave's mask of v, then read it back; a
+        // lane's rank is the number of set bits below it (one wave's LDS operations complete in
+        // order, so every read sees all the ORs, and the clear below comes after all reads).
+        uint64_t* mym = wmask + wave * E;
+        if (l >= 0) atomicOr(reinterpret_cast<unsigned long long*>(mym + l), 1ull << lane);
+        const uint64_t mv = l >= 0 ? mym[l] : 0ull;
+        rank = __popcll(mv & lt_mask);
+        same = __popcll(mv);
+        if (l >= 0 && rank == 0) mym[l] = 0ull;
+      } else {
+        while (todo) {
+          const int v = __builtin_amdgcn_readlane(l, __builtin_ctzll(todo));
+          const uint64_t mv = __ballot(l == v);
+          if (l == v) {
+            rank = __popcll(mv & lt_mask);
+            same = __popcll(mv);
+          }
+          todo &= ~mv;
         }
-        todo &= ~mv;
       }
       // Every lane reads the running count before the expert's first lane bumps it (one
       // wave's LDS operations complete in order).
@@ -419,14 +442,16 @@ __global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParam
 }
 
 size_t route_pack_lds_bytes(int num_experts, int64_t num_routes) {
-  return route_pack_base_lds(num_experts) +
-         (segmented_pack(num_routes, num_experts) ? size_t(kCacheRoutes) * 4 + size_t(kPackWaves) * num_experts * 2 : 0);
+  if (!segmented_pack(num_routes, num_experts)) return route_pack_base_lds(num_experts);
+  return route_pack_base_lds(num_experts) + size_t(kCacheRoutes) * 4 + (size_t(kPackWaves) * num_experts * 2 + 7) / 8 * 8 +
+         (mask_ranks(num_experts) ? size_t(kPackWaves) * num_experts * 8 : 0);
 }
 
 hipError_t launch_route_pack(const RoutePackParams& p, int side_blocks, hipStream_t stream) {
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_pack_kernel),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       int(route_pack_lds_bytes(kSegExperts, kCacheRoutes)));
+                                                       int(std::max(route_pack_lds_bytes(kSegExperts, kCacheRoutes),
+                                                                    route_pack_lds_bytes(kMaskExperts, kCacheRoutes))));
   if (lds_ok != hipSuccess) return lds_ok;
   const size_t lds = route_pack_lds_bytes(p.num_experts, p.num_routes);
   hipLaunchKernelGGL(route_pack_kernel, dim3(1 + (p.x16 ? side_blocks : 0)), dim3(kPackThreads), lds, stream, p);
