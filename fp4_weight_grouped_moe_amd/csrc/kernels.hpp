@@ -101,7 +101,7 @@ constexpr int kRouterMaxExperts = 1024;
 constexpr int kRouterMaxTopk = 64;
 hipError_t launch_router(const RouterParams& p, hipStream_t stream);
 
-size_t route_pack_lds_bytes(int num_experts, int64_t num_routes);
+size_t route_pack_lds_bytes(int num_experts, int64_t num_routes, int64_t cap_routes, int block_m);
 // `side_blocks` extra workgroups do the activation conversion when p.x16 is set.
 hipError_t launch_route_pack(const RoutePackParams& p, int side_blocks, hipStream_t stream);
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);

@@ -53,6 +53,27 @@ __host__ __device__ inline bool segmented_pack(int64_t num_routes, int num_exper
 constexpr int kMaskExperts = 256;
 __host__ __device__ inline bool mask_ranks(int num_experts) { return num_experts <= kMaskExperts; }
 
+// Segmented packs whose slot range fits in LDS as 16-bit route ids write the slot-ordered
+// tables (sorted route ids, token + weight per slot, padding included) in slot order, from a
+// slot -> route map built in LDS: coalesced stores instead of one cache line per route and per
+// padding slot (27 of the 56 us of a 16 384-route pack were those scattered stores). The map
+// sits after the cached ids and ranks, over the per-wave counts and lane masks, followed by
+// the block -> expert table (a block's first slot always holds a route: its expert is the
+// block's); the router weights are staged over the ids and ranks once those are in registers.
+constexpr size_t kPackLdsMax = 163840;
+constexpr int kRoutesPerThread = kCacheRoutes / kPackThreads;
+constexpr int kSlotBits = 17;                  // slot | local expert << kSlotBits in one register
+__host__ __device__ inline size_t slot_map_offset(int num_experts) {
+  return route_pack_base_lds(num_experts) + size_t(kCacheRoutes) * 4;
+}
+__host__ __device__ inline size_t block_map_offset(int num_experts, int64_t cap_routes) {
+  return slot_map_offset(num_experts) + (size_t(cap_routes) * 2 + 15) / 16 * 16;
+}
+__host__ __device__ inline bool slot_map_pass(int64_t num_routes, int num_experts, int64_t cap_routes, int block_m) {
+  return segmented_pack(num_routes, num_experts) && cap_routes < (int64_t(1) << kSlotBits) &&
+         block_map_offset(num_experts, cap_routes) + size_t(cap_routes / block_m) * 2 <= kPackLdsMax;
+}
+
 __device__ void cache_routes(const RoutePackParams& p, int16_t* lc, int* cnt) {
   const int tid = threadIdx.x;
   const int64_t R = p.num_routes;
@@ -149,6 +170,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   int* ecnt = wave_tot + 40;                               // [E] counts (kept for the tile table)
   uint8_t* wcnt = reinterpret_cast<uint8_t*>(ecnt + E);    // [kPackWaves][E] per-wave counts
   const bool cached = segmented_pack(p.num_routes, E);
+  const bool slot_pass = slot_map_pass(p.num_routes, E, p.cap_routes, B);
   int16_t* lc = reinterpret_cast<int16_t*>(smem + route_pack_base_lds(E));                          // [R] local ids
   uint16_t* srank = reinterpret_cast<uint16_t*>(smem + route_pack_base_lds(E) + size_t(kCacheRoutes) * 2);   // [R] rank in segment
   uint16_t* scnt = srank + kCacheRoutes;                                                            // [waves][E] counts, then bases
@@ -194,10 +216,12 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
     if (e < E) {
       p.expert_counts[e] = c;
       p.expert_offsets[e] = off;
-      for (int b = off / B; b < (off + padded) / B; ++b) p.block_expert[b] = e;
-      for (int s = off + c; s < off + padded; ++s) {
-        p.sorted_route_ids[s] = -1;
-        if (p.slot_info) p.slot_info[s] = make_int2(-1, 0);
+      if (!slot_pass) {
+        for (int b = off / B; b < (off + padded) / B; ++b) p.block_expert[b] = e;
+        for (int s = off + c; s < off + padded; ++s) {
+          p.sorted_route_ids[s] = -1;
+          if (p.slot_info) p.slot_info[s] = make_int2(-1, 0);
+        }
       }
       if (p.tiles) {
         for (int t = 0; t < nfull; ++t)
@@ -298,16 +322,69 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
       }
     }
     __syncthreads();
-    for (int r = tid; r < R; r += kPackThreads) {
-      const int l = lc[r];
-      if (l >= 0) {
-        const int pos = int(scnt[(r / S) * E + l]) + int(srank[r]);
-        p.sorted_route_ids[pos] = r;
-        p.route_slot[r] = pos;
-        if (p.slot_info)
-          p.slot_info[pos] = make_int2(r / p.topk, __float_as_int(p.topk_weights ? p.topk_weights[r] : 0.f));
-      } else {
-        p.route_slot[r] = -1;
+    if (slot_pass) {
+      // Each thread's routes' router weights (loads in flight meanwhile) and slots into
+      // registers (route order: coalesced route_slot), then the slot -> route map in LDS
+      // (0xFFFF: padding) with the block -> expert table, then one pass in slot order.
+      const bool wts = p.slot_info != nullptr;
+      float wreg[kRoutesPerThread];
+#pragma unroll
+      for (int k = 0; k < kRoutesPerThread; ++k) {
+        const int r = tid + k * kPackThreads;
+        wreg[k] = (wts && p.topk_weights && r < R) ? p.topk_weights[r] : 0.f;
+      }
+      int pos[kRoutesPerThread];
+#pragma unroll
+      for (int k = 0; k < kRoutesPerThread; ++k) {
+        const int r = tid + k * kPackThreads;
+        int q = -1;
+        if (r < R) {
+          const int l = lc[r];
+          if (l >= 0) q = int(scnt[(r / S) * E + l]) + int(srank[r]);
+          p.route_slot[r] = q;
+          if (l >= 0) q |= l << kSlotBits;
+        }
+        pos[k] = q;
+      }
+      __syncthreads();                                     // ids, ranks, counts and masks are free now
+      uint16_t* smap = reinterpret_cast<uint16_t*>(smem + slot_map_offset(E));                 // [total_padded]
+      uint16_t* bmap = reinterpret_cast<uint16_t*>(smem + block_map_offset(E, p.cap_routes));  // [total_padded / B]
+      float* wst = reinterpret_cast<float*>(smem + route_pack_base_lds(E));                     // [R] router weights
+      for (int s = tid; s < total_padded; s += kPackThreads) smap[s] = 0xFFFF;
+      if (wts) {
+#pragma unroll
+        for (int k = 0; k < kRoutesPerThread; ++k)
+          if (tid + k * kPackThreads < R) wst[tid + k * kPackThreads] = wreg[k];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kRoutesPerThread; ++k) {
+        if (pos[k] >= 0) {
+          const int q = pos[k] & ((1 << kSlotBits) - 1);
+          smap[q] = uint16_t(tid + k * kPackThreads);
+          if ((q & (B - 1)) == 0) bmap[q / B] = uint16_t(pos[k] >> kSlotBits);
+        }
+      }
+      __syncthreads();
+      for (int s = tid; s < total_padded; s += kPackThreads) {
+        const int v = smap[s];
+        const bool pad = v == 0xFFFF;
+        p.sorted_route_ids[s] = pad ? -1 : v;
+        if (wts) p.slot_info[s] = pad ? make_int2(-1, 0) : make_int2(v / p.topk, __float_as_int(wst[v]));
+      }
+      for (int b = tid; b < total_padded / B; b += kPackThreads) p.block_expert[b] = bmap[b];
+    } else {
+      for (int r = tid; r < R; r += kPackThreads) {
+        const int l = lc[r];
+        if (l >= 0) {
+          const int pos = int(scnt[(r / S) * E + l]) + int(srank[r]);
+          p.sorted_route_ids[pos] = r;
+          p.route_slot[r] = pos;
+          if (p.slot_info)
+            p.slot_info[pos] = make_int2(r / p.topk, __float_as_int(p.topk_weights ? p.topk_weights[r] : 0.f));
+        } else {
+          p.route_slot[r] = -1;
+        }
       }
     }
   }
@@ -441,19 +518,22 @@ __global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParam
   }
 }
 
-size_t route_pack_lds_bytes(int num_experts, int64_t num_routes) {
+size_t route_pack_lds_bytes(int num_experts, int64_t num_routes, int64_t cap_routes, int block_m) {
   if (!segmented_pack(num_routes, num_experts)) return route_pack_base_lds(num_experts);
-  return route_pack_base_lds(num_experts) + size_t(kCacheRoutes) * 4 + (size_t(kPackWaves) * num_experts * 2 + 7) / 8 * 8 +
-         (mask_ranks(num_experts) ? size_t(kPackWaves) * num_experts * 8 : 0);
+  const size_t ranks = route_pack_base_lds(num_experts) + size_t(kCacheRoutes) * 4 +
+                       (size_t(kPackWaves) * num_experts * 2 + 7) / 8 * 8 +
+                       (mask_ranks(num_experts) ? size_t(kPackWaves) * num_experts * 8 : 0);
+  const size_t map = slot_map_pass(num_routes, num_experts, cap_routes, block_m)
+                         ? (block_map_offset(num_experts, cap_routes) + size_t(cap_routes / block_m) * 2 + 15) / 16 * 16
+                         : 0;
+  return std::max(ranks, map);
 }
 
 hipError_t launch_route_pack(const RoutePackParams& p, int side_blocks, hipStream_t stream) {
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_pack_kernel),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       int(std::max(route_pack_lds_bytes(kSegExperts, kCacheRoutes),
-                                                                    route_pack_lds_bytes(kMaskExperts, kCacheRoutes))));
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(kPackLdsMax));
   if (lds_ok != hipSuccess) return lds_ok;
-  const size_t lds = route_pack_lds_bytes(p.num_experts, p.num_routes);
+  const size_t lds = route_pack_lds_bytes(p.num_experts, p.num_routes, p.cap_routes, p.block_m);
   hipLaunchKernelGGL(route_pack_kernel, dim3(1 + (p.x16 ? side_blocks : 0)), dim3(kPackThreads), lds, stream, p);
   return hipGetLastError();
 }
