@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--w4a8", action="store_true",
                     help="time the W4A8 variant (moe_w4a8_fused, MXFP4 workloads): whole-layer time only")
+    ap.add_argument("--atomic-bf16", action="store_true",
+                    help="time the opt-in packed-bf16 atomic top-k combine (moe_w4a16_fused_atomic_bf16): "
+                         "whole-layer time only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run three device copies of MIB MiB (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -187,7 +190,8 @@ def main():
     tail = (k, moe._ptr(d_map), cfg.num_global_experts, cap, moe._ptr(layer.workspace), layer.workspace_bytes,
             moe._ptr(out), stream)
 
-    fused = lib.moe_w4a8_fused if args.w4a8 else lib.moe_w4a16_fused
+    fused = lib.moe_w4a8_fused if args.w4a8 else (lib.moe_w4a16_fused_atomic_bf16 if args.atomic_bf16 else lib.moe_w4a16_fused)
+    whole_only = args.w4a8 or args.atomic_bf16      # the measurement twin runs the W4A16 layer
 
     def step(i, events=None):
         px, pi, pw = ptrs[i % sets]
@@ -215,7 +219,7 @@ def main():
     # measurement twin runs the W4A16 layer, so the W4A8 line reports the whole layer only)
     names = ["route_pack", "fc1", "fc2", "combine"]
     per = {n: 0.0 for n in names}
-    if not args.w4a8:
+    if not whole_only:
         hev = HipEvents(5 * args.steps)
         for i in range(args.steps):
             step(args.warmup + i, [hev.ev[5 * i + j] for j in range(5)])
@@ -236,7 +240,7 @@ def main():
     t = ms_per_step * 1e-3
     decode_path = args.path == "decode" or (args.path == "auto" and m <= moe.MOE_DECODE_MAX_M and cap <= moe.MOE_DECODE_MAX_M)
     kernel_src = "decode.hip" if decode_path else "gemm.hip"
-    if args.w4a8:
+    if whole_only:
         roof = None
     elif decode_path:
         # dominant kernel: FC1 (W13 is two thirds of the streamed weights)
@@ -273,20 +277,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: E{cfg.num_experts} H{H} I{cfg.inter} top{k} {cfg.fmt.upper()} "
                                f"{cfg.act} m={m}", "m": m, "token_capacity": cap, "routing_sets": sets,
-                   "path": "decode" if decode_path else "gemm", "variant": "w4a8" if args.w4a8 else "w4a16"},
+                   "path": "decode" if decode_path else "gemm", "variant": "w4a8" if args.w4a8 else ("w4a16-atomic-bf16" if args.atomic_bf16 else "w4a16")},
         "effective_weight_GBps": round(weight_bytes / t / 1e9, 1),
         "weight_hbm_frac": round(weight_bytes / t / 1e9 / HBM_PEAK_GBPS, 4),
         "layer_bytes_per_step": int(step_bytes),
         "tflops": round(flops / t / 1e12, 3),
         "mfma_frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 5),
         "touched_experts_avg": round(avg_touched, 2),
-        "kernel_us": None if args.w4a8 else {n: round(v * 1e3, 2) for n, v in per.items()},
+        "kernel_us": None if whole_only else {n: round(v * 1e3, 2) for n, v in per.items()},
         "roofline": roof,
     }
     del codes
     torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline and not args.w4a8:
+    if not args.no_cpu_baseline and not whole_only:
         res["cpu_baseline"] = cpu_baseline(cfg, ids_l, w_l, x_l, emap, dev, m, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 

@@ -81,6 +81,7 @@ def _load():
         "moe_w4a16_workspace_size": (I32, [PD, I64, I32, PSZ]),
         "moe_w4a16_fused": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
         "moe_w4a8_fused": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
+        "moe_w4a16_fused_atomic_bf16": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
         "moe_w4a16_fused_profiled": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P, P, I32]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_w4a16_set_path": (I32, [I32]),
@@ -98,7 +99,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("moe_route_pack_token_capacity", "moe_route_pack_workspace_size", "moe_route_pack",
             "moe_w4a16_prepared_size", "moe_w4a16_prepare", "moe_w4a16_workspace_size", "moe_w4a16_fused",
-            "moe_w4a8_fused",
+            "moe_w4a8_fused", "moe_w4a16_fused_atomic_bf16",
             "moe_w4a16_fused_profiled", "moe_last_error", "moe_w4a16_set_path", "moe_w4a16_set_decode_max_m",
             "moe_router_topk", "moe_w4a16_prepare_layout")
 
@@ -196,6 +197,15 @@ def moe_w4a8_fused(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: in
                                _ptr(workspace), workspace_bytes, _ptr(out), _stream(stream)), "moe_w4a8_fused")
 
 
+def moe_w4a16_fused_atomic_bf16(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: int, topk_ids,
+                                topk_weights, topk: int, expert_map, num_global_experts: int, token_capacity: int,
+                                workspace, workspace_bytes: int, out, stream=None) -> None:
+    _check(_lib.moe_w4a16_fused_atomic_bf16(ctypes.byref(dims), _ptr(prepared), prepared_bytes, _ptr(x), m,
+                                            _ptr(topk_ids), _ptr(topk_weights), topk, _ptr(expert_map),
+                                            num_global_experts, token_capacity, _ptr(workspace), workspace_bytes,
+                                            _ptr(out), _stream(stream)), "moe_w4a16_fused_atomic_bf16")
+
+
 def moe_w4a16_fused_profiled(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: int, topk_ids, topk_weights,
                              topk: int, expert_map, num_global_experts: int, token_capacity: int, workspace,
                              workspace_bytes: int, out, events, stream=None) -> None:
@@ -251,15 +261,18 @@ class MoeLayer:
         moe_w4a16_prepare(self.dims, w13, s13, g13, w2, s2, g2, self.prepared, self.prepared_bytes, stream)
 
     def __call__(self, x, topk_ids, topk_weights, expert_map=None, num_global_experts=None, out=None, stream=None,
-                 w4a8=False):
-        """``w4a8``: the W4A8 variant (moe_w4a8_fused; MXFP4 weights only)."""
+                 w4a8=False, atomic_bf16=False):
+        """``w4a8``: the W4A8 variant (moe_w4a8_fused; MXFP4 weights only). ``atomic_bf16``: the
+        opt-in approximate packed-bf16 atomic top-k combine (moe_w4a16_fused_atomic_bf16)."""
+        if w4a8 and atomic_bf16:
+            raise ValueError("w4a8 and atomic_bf16 are separate variants")
         import torch
         m = int(x.shape[0])
         if out is None:
             out = torch.empty((m, self.dims.hidden), dtype=torch.bfloat16, device=x.device)
         ng = num_global_experts if num_global_experts is not None else (
             int(expert_map.numel()) if expert_map is not None else self.dims.num_experts)
-        fn = moe_w4a8_fused if w4a8 else moe_w4a16_fused
+        fn = moe_w4a8_fused if w4a8 else (moe_w4a16_fused_atomic_bf16 if atomic_bf16 else moe_w4a16_fused)
         fn(self.dims, self.prepared, self.prepared_bytes, x, m, topk_ids, topk_weights, self.topk,
            expert_map, ng, self.token_capacity, self.workspace, self.workspace_bytes, out, stream)
         return out

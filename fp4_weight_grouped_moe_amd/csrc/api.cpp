@@ -251,7 +251,7 @@ namespace {
 int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes, const uint16_t* x, int64_t m,
                const int32_t* topk_ids, const float* topk_weights, int topk, const int32_t* expert_map,
                int num_global_experts, int64_t token_capacity, void* workspace, size_t workspace_bytes, uint16_t* out,
-               hipStream_t stream, hipEvent_t* events, bool w4a8 = false) {
+               hipStream_t stream, hipEvent_t* events, bool w4a8 = false, bool atomic_bf16 = false) {
   if (int rc = check_dims(dims)) return rc;
   if (w4a8 && dims->fmt != MOE_FMT_MXFP4_E8M0_K32)
     return fail(MOE_ERR_UNSUPPORTED, "the W4A8 variant needs MXFP4 weights (E8M0 block scales)");
@@ -349,6 +349,7 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   fp.f2_count = decode ? reinterpret_cast<int32_t*>(ws + fg.off_count) : nullptr;
   fp.cap_blocks = pg.cap_blocks;
   fp.w4a8 = w4a8 ? 1 : 0;
+  fp.atomic_bf16 = atomic_bf16 && !decode ? 1 : 0;
   fp.inter32 = w4a8 ? reinterpret_cast<float*>(ws + fg.off_inter32) : nullptr;
   fp.inter8 = w4a8 && decode ? ws + fg.off_inter8 : nullptr;
   fp.sc8 = w4a8 && decode ? ws + fg.off_sc8 : nullptr;
@@ -390,6 +391,14 @@ int moe_w4a8_fused(const moe_w4a16_dims* dims, const void* prepared, size_t prep
                    size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
   return fused_impl(dims, prepared, prepared_bytes, x, m, topk_ids, topk_weights, topk, expert_map,
                     num_global_experts, token_capacity, workspace, workspace_bytes, out, stream, nullptr, true);
+}
+
+int moe_w4a16_fused_atomic_bf16(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes,
+                                const uint16_t* x, int64_t m, const int32_t* topk_ids, const float* topk_weights,
+                                int topk, const int32_t* expert_map, int num_global_experts, int64_t token_capacity,
+                                void* workspace, size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
+  return fused_impl(dims, prepared, prepared_bytes, x, m, topk_ids, topk_weights, topk, expert_map,
+                    num_global_experts, token_capacity, workspace, workspace_bytes, out, stream, nullptr, false, true);
 }
 
 int moe_w4a16_fused_profiled(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes,

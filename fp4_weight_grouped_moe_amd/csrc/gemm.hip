@@ -312,6 +312,28 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
         }
       }
     }
+  } else if (p.atomic_bf16) {
+    // Opt-in approximate top-k sum: each route's row (router weight and FC2 global scale
+    // already folded in by FC1) rounded to bf16 and added into its token's output row by
+    // packed-bf16 atomics; the sum's rounding and order vary from run to run.
+#pragma unroll
+    for (int bb = 0; bb < BW; ++bb) {
+      const int b = bb;
+      if (b < nb) {
+        const int tok = p.slot_info[(fb + b) * kBlockM + col].x;
+        if (tok >= 0) {
+#pragma unroll
+          for (int f = 0; f < FR; ++f) {
+            const int64_t h = int64_t(rg_base + f) * 16 + r0;
+            if (h < g.H) {
+              bf16x2* dst = reinterpret_cast<bf16x2*>(p.out + int64_t(tok) * g.H + h);
+              __builtin_amdgcn_global_atomic_fadd_v2bf16(dst, __builtin_bit_cast(bf16x2, pack_bf16x2(acc[f][bb][0], acc[f][bb][1])));
+              __builtin_amdgcn_global_atomic_fadd_v2bf16(dst + 1, __builtin_bit_cast(bf16x2, pack_bf16x2(acc[f][bb][2], acc[f][bb][3])));
+            }
+          }
+        }
+      }
+    }
   } else {
 #pragma unroll
     for (int bb = 0; bb < BW; ++bb) {
@@ -350,6 +372,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
     c.act_row_bytes = int(g.ip * 2);
     c.k_bytes = int(g.ip * 2);
     c.act = __builtin_amdgcn_make_buffer_rsrc(p.inter, 0, int(p.cap_blocks * kBlockM * g.ip * 2), 0x00020000);
+  }
+  if (PHASE == 1 && p.atomic_bf16) {
+    // FC2 accumulates into the output with atomics: zero it first (m * H * 2 bytes, H % 8 == 0;
+    // FC2 runs after this launch in stream order).
+    const int64_t n16 = p.m * g.H / 8;
+    u32x4* o = reinterpret_cast<u32x4*>(p.out);
+    for (int64_t i = int64_t(blockIdx.x) * kGemmThreads + threadIdx.x; i < n16; i += int64_t(gridDim.x) * kGemmThreads)
+      o[i] = u32x4{0u, 0u, 0u, 0u};
   }
   const int n_mt = p.live[4];
   const int n_nt = (c.groups + 15) / 16;
@@ -449,7 +479,7 @@ hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hi
   if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   if (marks) (void)hipEventRecord(marks[1], stream);
-  launch_combine(p, stream);
+  if (!p.atomic_bf16) launch_combine(p, stream);
   if (marks) (void)hipEventRecord(marks[2], stream);
   return hipGetLastError();
 }

@@ -74,6 +74,9 @@ struct FusedParams {
   // rows are rounded to MXFP8 in place (launch_mxfp8_requant), and FC2 applies router weight x
   // FC2 global scale per route.
   int32_t w4a8;
+  // Grouped-GEMM path, opt-in: FC2 adds each route's weighted row into the bf16 output with
+  // packed-bf16 atomics (FC1 zeroes the output first); no fp32 rows, no combine pass.
+  int32_t atomic_bf16;
   float* inter32;                // W4A8: fp32 [cap_routes, ip] activation output of FC1
   uint8_t* inter8;               // W4A8, decode path: MXFP8 codes [cap_routes, ip] (E4M3)
   uint8_t* sc8;                  //   and their E8M0 scales [cap_routes, ip / 32]

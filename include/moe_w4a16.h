@@ -198,13 +198,32 @@ int moe_w4a16_fused(const moe_w4a16_dims* dims, const void* prepared, size_t pre
  * out[t] = sum_j w[t, j] * W2_e @ MXFP8(act(W13_e @ x_t)) over surviving routes.
  * Arguments, layouts, ownership and errors as moe_w4a16_fused (same prepared buffer and
  * workspace); MOE_ERR_UNSUPPORTED unless dims->fmt is MOE_FMT_MXFP4_E8M0_K32 (the gfx950
- * block-scaled MFMA applies E8M0 scales only). The GPU rounds the bf16 activation output
- * (the W4A16 intermediate) and FC2 multiplies the exact MXFP8 values on the bf16 MFMA. */
+ * block-scaled MFMA applies E8M0 scales only). FC1 keeps the activation output in fp32 for
+ * the rounding (one rounding, as defined); the decode path's FC2 multiplies the E4M3 codes on
+ * gfx950's block-scaled FP4 x FP8 MFMA, the grouped-GEMM path's the exact MXFP8 values on the
+ * bf16 MFMA. */
 int moe_w4a8_fused(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes,
                    const uint16_t* x, int64_t m, const int32_t* topk_ids,
                    const float* topk_weights, int topk, const int32_t* expert_map,
                    int num_global_experts, int64_t token_capacity, void* workspace,
                    size_t workspace_bytes, uint16_t* out, hipStream_t stream);
+
+/* Opt-in approximate top-k combine. Page: the FlashInfer fused-MoE kernel source's atomic
+ * reduction helpers (a bf16 scatter-add, f32 rounded to bf16 to nearest and then added
+ * atomically, offered as an opt-in approximate mode beside the f32 reduction). The same layer
+ * as moe_w4a16_fused; on the grouped-GEMM path (m above the decode threshold) FC2 rounds each
+ * route's weighted row to bf16 and adds it into its token's output row with gfx950's
+ * packed-bf16 global atomic (FC1 zeroes `out` first), instead of writing fp32 rows for the
+ * fixed-order combine pass. Every partial sum is rounded to bf16 and the order of the adds
+ * varies, so results can differ from run to run and from moe_w4a16_fused by a few bf16 ulps
+ * of the row's magnitude. On the decode path it is moe_w4a16_fused exactly (that path sums
+ * the top-k in registers). Arguments, layouts, ownership and errors as moe_w4a16_fused. */
+int moe_w4a16_fused_atomic_bf16(const moe_w4a16_dims* dims, const void* prepared,
+                                size_t prepared_bytes, const uint16_t* x, int64_t m,
+                                const int32_t* topk_ids, const float* topk_weights, int topk,
+                                const int32_t* expert_map, int num_global_experts,
+                                int64_t token_capacity, void* workspace, size_t workspace_bytes,
+                                uint16_t* out, hipStream_t stream);
 
 /* ------------------------------------------------------------------ diagnostics */
 

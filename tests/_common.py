@@ -111,12 +111,12 @@ def make_layer(case: Case, device, token_capacity: Optional[int] = None):
     return layer
 
 
-def run_layer(layer, case: Case, device, out=None, w4a8=False):
+def run_layer(layer, case: Case, device, out=None, w4a8=False, atomic_bf16=False):
     import torch
 
     x = dev(case.xbits.view(np.int16), device).view(torch.bfloat16)
     emap = dev(case.emap, device) if case.emap is not None else None
     out = layer(x, dev(case.ids, device), dev(case.w, device), expert_map=emap,
-                num_global_experts=case.cfg.num_global_experts, out=out, w4a8=w4a8)
+                num_global_experts=case.cfg.num_global_experts, out=out, w4a8=w4a8, atomic_bf16=atomic_bf16)
     torch.cuda.synchronize()
     return out
