@@ -577,6 +577,7 @@ typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 template <int FMT, int RG, bool W8>
 __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedParams p) {
+  static_assert(!W8 || kF3KB == 2, "the block-scaled FC2 takes one 128-K block pair (256 codes) per workgroup");
   extern __shared__ __align__(16) uint8_t dyn[];
   const PreparedGeom& g = p.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
