@@ -313,8 +313,10 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
     }
     __syncthreads();
     // Segment bases: expert e's slots for wave w start after the earlier waves' routes of e.
+    // Kept relative to the expert's padded offset cnt[e] (below kCacheRoutes, so 16 bits
+    // hold them; the offsets themselves reach cap_routes, beyond 16 bits for large E x B).
     for (int e = tid; e < E; e += kPackThreads) {
-      int run = cnt[e];
+      int run = 0;
       for (int w2 = 0; w2 < kPackWaves; ++w2) {
         const int c = scnt[w2 * E + e];
         scnt[w2 * E + e] = uint16_t(run);
@@ -340,7 +342,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
         int q = -1;
         if (r < R) {
           const int l = lc[r];
-          if (l >= 0) q = int(scnt[(r / S) * E + l]) + int(srank[r]);
+          if (l >= 0) q = cnt[l] + int(scnt[(r / S) * E + l]) + int(srank[r]);
           p.route_slot[r] = q;
           if (l >= 0) q |= l << kSlotBits;
         }
@@ -377,7 +379,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
       for (int r = tid; r < R; r += kPackThreads) {
         const int l = lc[r];
         if (l >= 0) {
-          const int pos = int(scnt[(r / S) * E + l]) + int(srank[r]);
+          const int pos = cnt[l] + int(scnt[(r / S) * E + l]) + int(srank[r]);
           p.sorted_route_ids[pos] = r;
           p.route_slot[r] = pos;
           if (p.slot_info)

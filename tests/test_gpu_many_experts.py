@@ -1,0 +1,107 @@
+"""Route packing and the fused layer with more than 256 local experts (GPU).
+
+Above 256 experts the segmented pack ranks each 64-route chunk with one ballot pass per
+distinct expert instead of per-wave lane masks, and the slot-ordered tables are written from
+an LDS slot -> route map only while that map fits (else by the route-order scatter). The
+route pack must match the oracle bit for bit (FlashInfer PR 4255, Description and Tests:
+shape-stable packing, expert_map, invalid ids); the fused layer within the usual bf16
+tolerance, max|gpu - oracle| <= 2e-2 max|oracle| + 1e-3.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from _common import bf16_tensor_to_f64, dev, make_case, make_layer, oracle_out, run_layer
+from oracle import moe as M
+from oracle import route_pack as RP
+from synth import configs as C
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    d = torch.device("cuda:0")
+    torch.cuda.set_device(d)
+    return d
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import fp4_weight_grouped_moe_amd as m
+    yield m
+    m.moe_w4a16_set_path("auto")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# (local experts, global experts, expert_map?, m, k, block_m): 1 025 - 16 384 routes (the
+# segmented pack); B = 64 with 1 024 experts overflows the LDS slot map (route-order scatter).
+MANY = [(300, 300, False, 512, 8, 16), (1024, 2048, True, 2048, 8, 16), (1024, 1024, False, 2048, 8, 64),
+        (600, 600, False, 1000, 6, 32), (257, 257, False, 171, 6, 128)]
+
+
+@pytest.mark.parametrize("E,Eg,use_map,m,k,B", MANY)
+def test_route_pack_many_experts_bit_exact(moe, device, E, Eg, use_map, m, k, B):
+    rng = np.random.default_rng(E * 7 + m + B)
+    ids = rng.integers(-2, Eg + 3, size=(m, k)).astype(np.int32)        # -1, -2 and out-of-range ids too
+    ids[rng.random((m, k)) < 0.3] = int(rng.integers(0, 4))             # a few heavy experts
+    emap = None
+    if use_map:
+        emap = np.full(Eg, -1, np.int32)
+        keep = rng.permutation(Eg)[:E]
+        emap[keep] = np.arange(E, dtype=np.int32)
+    cap = RP.token_capacity(m)
+    _say(f"route_pack E={E} Eg={Eg} map={use_map} m={m} k={k} B={B}")
+    nbytes = moe.moe_route_pack_workspace_size(cap, k, E, B)
+    ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device=device)
+    d_ids = dev(ids, device)
+    d_map = dev(emap, device) if emap is not None else None
+    view = moe.moe_route_pack(d_ids, m, k, d_map, Eg, E, B, cap, ws, nbytes)
+    torch.cuda.synchronize()
+    base = ws.data_ptr()
+
+    def read(ptr, n):
+        off = ptr - base
+        return ws[off:off + 4 * n].view(torch.int32).cpu().numpy().copy()
+
+    got = {
+        "expert_counts": read(view.expert_counts, E),
+        "expert_offsets": read(view.expert_offsets, E + 1),
+        "sorted_route_ids": read(view.sorted_route_ids, view.cap_routes),
+        "block_expert": read(view.block_expert, view.cap_blocks),
+        "live": read(view.live, 4),
+        "route_slot": read(view.route_slot, cap * k),
+    }
+    want = RP.route_pack(ids, emap, Eg, E, B, cap)
+    for key in want:
+        assert np.array_equal(got[key], want[key]), key
+
+
+FUSED_MANY = [
+    (C.scaled(C.get_config("prefill"), num_experts=512, hidden=256, inter=128, name="prefill_e512"), 1024, "normal"),
+    (C.scaled(C.get_config("edge"), num_experts=1024, num_global_experts=2048, hidden=256, inter=200,
+              name="edge_e1024"), 512, "random"),
+]
+
+
+@pytest.mark.parametrize("cfg,m,weights", FUSED_MANY, ids=lambda v: getattr(v, "name", str(v)))
+def test_fused_many_experts_matches_oracle(moe, device, cfg, m, weights):
+    _say(f"fused {cfg.name} m={m}")
+    case = make_case(cfg, m, seed=cfg.index * 31 + m, weights=weights)
+    layer = make_layer(case, device)
+    got = bf16_tensor_to_f64(run_layer(layer, case, device))
+    ref = oracle_out(case)
+    ok, err, bound = M.within_tolerance(got, ref)
+    _say(f"  max|err| = {err:.3e}, bound = {bound:.3e}")
+    assert ok, f"{cfg.name} m={m}: {err} > {bound}"
+    del layer
+    torch.cuda.empty_cache()
