@@ -1,4 +1,5 @@
-"""Route packing and the fused layer with more than 256 local experts (GPU).
+"""Route packing and the fused layer with more than 256 local experts or more than 16 384
+routes (GPU).
 
 Above 256 experts the segmented pack ranks each 64-route chunk with one ballot pass per
 distinct expert instead of per-wave lane masks, and the slot-ordered tables are written from
@@ -44,9 +45,12 @@ def _say(msg):
 
 
 # (local experts, global experts, expert_map?, m, k, block_m): 1 025 - 16 384 routes (the
-# segmented pack); B = 64 with 1 024 experts overflows the LDS slot map (route-order scatter).
+# segmented pack); B = 64 with 1 024 experts overflows the LDS slot map (route-order scatter);
+# above 16 384 routes the pack runs 1 024-route chunks with running per-expert slots.
 MANY = [(300, 300, False, 512, 8, 16), (1024, 2048, True, 2048, 8, 16), (1024, 1024, False, 2048, 8, 64),
-        (600, 600, False, 1000, 6, 32), (257, 257, False, 171, 6, 128)]
+        (600, 600, False, 1000, 6, 32), (257, 257, False, 171, 6, 128),
+        (256, 256, False, 4096, 8, 16), (64, 128, True, 3001, 6, 128), (2048, 2048, False, 2100, 8, 32),
+        (2048, 2048, False, 100, 8, 16), (1500, 1500, False, 700, 7, 64)]   # above 1 024 experts: chunked
 
 
 @pytest.mark.parametrize("E,Eg,use_map,m,k,B", MANY)
@@ -88,6 +92,7 @@ def test_route_pack_many_experts_bit_exact(moe, device, E, Eg, use_map, m, k, B)
 
 FUSED_MANY = [
     (C.scaled(C.get_config("prefill"), num_experts=512, hidden=256, inter=128, name="prefill_e512"), 1024, "normal"),
+    (C.scaled(C.get_config("prefill"), num_experts=64, hidden=256, inter=128, name="prefill_m4096"), 4096, "normal"),
     (C.scaled(C.get_config("edge"), num_experts=1024, num_global_experts=2048, hidden=256, inter=200,
               name="edge_e1024"), 512, "random"),
 ]
