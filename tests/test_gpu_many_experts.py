@@ -110,3 +110,39 @@ def test_fused_many_experts_matches_oracle(moe, device, cfg, m, weights):
     assert ok, f"{cfg.name} m={m}: {err} > {bound}"
     del layer
     torch.cuda.empty_cache()
+
+
+def _decode_cfg(base, **kw):
+    import dataclasses
+    return dataclasses.replace(base, **kw)
+
+
+DECODE_MANY = [
+    (_decode_cfg(C.get_config("decode"), num_experts=2048, num_global_experts=2048, hidden=256, inter=128,
+                 name="decode_e2048"), (1, 8, 16)),
+    (_decode_cfg(C.get_config("edge"), num_experts=1500, num_global_experts=3000, hidden=256, inter=200,
+                 name="edge_e1500_map"), (8,)),
+    (_decode_cfg(C.get_config("decode"), num_experts=128, num_global_experts=128, hidden=256, inter=128, topk=64,
+                 name="decode_top64"), (1, 4, 8, 16)),
+]
+
+
+@pytest.mark.parametrize("cfg,ms", DECODE_MANY, ids=lambda v: getattr(v, "name", str(v)))
+def test_decode_path_many_experts_and_large_topk(moe, device, cfg, ms):
+    """Decode path (m <= 16): FC1's own route pack up to 2 048 experts and 256 routes (one per
+    thread), the separate pack launch and the one-pass FC2 beyond 128 routes (top-64 at
+    m = 4 .. 16); an expert_map over 3 000 global ids with 5 % invalid ids."""
+    moe.moe_w4a16_set_path("decode")
+    try:
+        for m in ms:
+            _say(f"decode {cfg.name} m={m}")
+            case = make_case(cfg, m, seed=cfg.index * 37 + m, weights="random")
+            layer = make_layer(case, device)
+            got = bf16_tensor_to_f64(run_layer(layer, case, device))
+            ok, err, bound = M.within_tolerance(got, oracle_out(case))
+            _say(f"  max|err| = {err:.3e}, bound = {bound:.3e}")
+            assert ok, f"{cfg.name} m={m}: {err} > {bound}"
+            del layer
+    finally:
+        moe.moe_w4a16_set_path("auto")
+    torch.cuda.empty_cache()
