@@ -146,3 +146,32 @@ def test_decode_path_many_experts_and_large_topk(moe, device, cfg, ms):
     finally:
         moe.moe_w4a16_set_path("auto")
     torch.cuda.empty_cache()
+
+
+ODD_DIMS = [
+    # (base workload, hidden, inter): hidden not a multiple of 128 (FC1 K tail, FC2's last row
+    # group partial; NVFP4 hidden 200 also ends in an 8-wide scale group), inter tails too
+    ("decode", 200, 136), ("decode", 1000, 232), ("small", 264, 100), ("edge", 200, 72), ("edge", 1000, 1400),
+]
+
+
+@pytest.mark.parametrize("base,H,I", ODD_DIMS)
+@pytest.mark.parametrize("path,m", [("decode", 3), ("decode", 16), ("gemm", 40)])
+def test_fused_hidden_not_a_multiple_of_128(moe, device, base, H, I, path, m):
+    import dataclasses
+    ref_cfg = C.get_config(base)
+    cfg = dataclasses.replace(ref_cfg, num_experts=8, num_global_experts=16 if ref_cfg.use_expert_map else 8,
+                              hidden=H, inter=I, name=f"{base}_h{H}_i{I}")
+    _say(f"{cfg.name} {cfg.fmt} {cfg.act} m={m} path={path}")
+    case = make_case(cfg, m, seed=H * 7 + I + m, weights="normal")
+    layer = make_layer(case, device)
+    moe.moe_w4a16_set_path(path)
+    try:
+        got = bf16_tensor_to_f64(run_layer(layer, case, device))
+    finally:
+        moe.moe_w4a16_set_path("auto")
+    ok, err, bound = M.within_tolerance(got, oracle_out(case))
+    _say(f"  max|err| = {err:.3e}, bound = {bound:.3e}")
+    assert ok, f"{cfg.name} m={m} {path}: {err} > {bound}"
+    del layer
+    torch.cuda.empty_cache()
