@@ -175,3 +175,26 @@ def test_fused_hidden_not_a_multiple_of_128(moe, device, base, H, I, path, m):
     assert ok, f"{cfg.name} m={m} {path}: {err} > {bound}"
     del layer
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("H,I", [(200, 72), (1000, 1400), (264, 136)])
+@pytest.mark.parametrize("path,m", [("decode", 3), ("decode", 16), ("gemm", 40)])
+def test_w4a8_hidden_not_a_multiple_of_128(moe, device, H, I, path, m):
+    """The W4A8 variant (MXFP8 activation output, block-scaled FC2 on the decode path) at the
+    same odd shapes, against the oracle's W4A8 forward."""
+    import dataclasses
+    cfg = dataclasses.replace(C.get_config("edge"), num_experts=8, num_global_experts=16, hidden=H, inter=I,
+                              name=f"edge_w4a8_h{H}_i{I}")
+    _say(f"{cfg.name} m={m} path={path}")
+    case = make_case(cfg, m, seed=H * 11 + I + m, weights="normal")
+    layer = make_layer(case, device)
+    moe.moe_w4a16_set_path(path)
+    try:
+        got = bf16_tensor_to_f64(run_layer(layer, case, device, w4a8=True))
+    finally:
+        moe.moe_w4a16_set_path("auto")
+    ok, err, bound = M.within_tolerance(got, oracle_out(case, mxfp8=True))
+    _say(f"  max|err| = {err:.3e}, bound = {bound:.3e}")
+    assert ok, f"{cfg.name} m={m} {path}: {err} > {bound}"
+    del layer
+    torch.cuda.empty_cache()
