@@ -198,3 +198,22 @@ def test_w4a8_hidden_not_a_multiple_of_128(moe, device, H, I, path, m):
     assert ok, f"{cfg.name} m={m} {path}: {err} > {bound}"
     del layer
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,m,cap", [("decode_s", 1, 16), ("decode_s", 5, 16), ("prefill_s", 17, 8192),
+                                        ("edge_s", 3, 1024), ("small_s", 64, 4096)])
+def test_fused_capacity_far_above_m(moe, device, name, m, cap):
+    """A workspace sized for far more tokens than the call has: the auto path takes the decode
+    kernels only while the capacity is at most 16, otherwise the grouped GEMM over a mostly
+    empty route space (padding slots, -1 block ids, empty tile queues)."""
+    from _common import SCALED
+    cfg = SCALED[name]
+    _say(f"capacity {name} m={m} cap={cap}")
+    case = make_case(cfg, m, seed=cfg.index * 41 + m, weights="normal")
+    layer = make_layer(case, device, token_capacity=cap)
+    got = bf16_tensor_to_f64(run_layer(layer, case, device))
+    ok, err, bound = M.within_tolerance(got, oracle_out(case))
+    _say(f"  max|err| = {err:.3e}, bound = {bound:.3e}")
+    assert ok, f"{name} m={m} cap={cap}: {err} > {bound}"
+    del layer
+    torch.cuda.empty_cache()
