@@ -92,3 +92,30 @@ def test_prepare_layout_rejects_bad_flags(moe, device):
     buf = torch.empty(size, dtype=torch.uint8, device=device)
     with pytest.raises(moe.MoeError):
         moe.moe_w4a16_prepare_layout(dims, moe.moe_w4a16_source_layout(2, 0, 0), buf, buf, buf, buf, buf, buf, buf, size)
+
+
+def _odd(base, H, I):
+    import dataclasses
+
+    from synth import configs as C
+    return dataclasses.replace(C.get_config(base), num_experts=4, num_global_experts=8 if base == "edge" else 4,
+                               hidden=H, inter=I, name=f"{base}_h{H}_i{I}")
+
+
+ODD = [_odd("decode", 200, 136), _odd("small", 264, 100), _odd("edge", 1000, 72)]
+
+
+@pytest.mark.parametrize("cfg", ODD, ids=lambda c: c.name)
+@pytest.mark.parametrize("up_first,reciprocal,per_row", [(1, 0, 0), (0, 1, 1), (1, 1, 1)])
+def test_prepare_layout_equals_canonical_odd_shapes(moe, device, cfg, up_first, reciprocal, per_row):
+    """The same at hidden sizes that are not a multiple of 128 (K tails and, for NVFP4 at
+    hidden 200, an 8-wide last scale group) and intermediate tails."""
+    print(f"layout {cfg.name} up_first={up_first} reciprocal={reciprocal} per_row={per_row}", flush=True)
+    var = _variant(cfg, 91 + 8 * up_first + 4 * reciprocal + 2 * per_row, up_first, reciprocal, per_row)
+    canon = L.canonical(cfg.fmt, cfg.act, cfg.hidden, cfg.inter, *var, w13_up_first=bool(up_first),
+                        global_scale_reciprocal=bool(reciprocal), scale_per_row=bool(per_row))
+    layout = moe.moe_w4a16_source_layout(up_first, reciprocal, per_row)
+    got = _prepare(moe, device, cfg, var, layout)
+    want = _prepare(moe, device, cfg, canon, None)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} prepared bytes differ, first at {bad[:8]}"
