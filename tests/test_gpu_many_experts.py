@@ -50,7 +50,11 @@ def _say(msg):
 MANY = [(300, 300, False, 512, 8, 16), (1024, 2048, True, 2048, 8, 16), (1024, 1024, False, 2048, 8, 64),
         (600, 600, False, 1000, 6, 32), (257, 257, False, 171, 6, 128),
         (256, 256, False, 4096, 8, 16), (64, 128, True, 3001, 6, 128), (2048, 2048, False, 2100, 8, 32),
-        (2048, 2048, False, 100, 8, 16), (1500, 1500, False, 700, 7, 64)]   # above 1 024 experts: chunked
+        (2048, 2048, False, 100, 8, 16), (1500, 1500, False, 700, 7, 64),   # above 1 024 experts: chunked
+        # route counts at the mode boundaries: one chunk (1 024), segmented (1 025, 16 384),
+        # chunked (16 392, 16 385)
+        (64, 64, False, 128, 8, 16), (64, 64, False, 1025, 1, 32), (200, 200, False, 2048, 8, 128),
+        (200, 200, False, 2049, 8, 16), (96, 96, False, 16385, 1, 64), (1024, 1024, False, 0, 4, 16)]
 
 
 @pytest.mark.parametrize("E,Eg,use_map,m,k,B", MANY)
