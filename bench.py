@@ -1,15 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of the fused W4A16 MoE layer on one MI355X.
 
-A step is one call of moe_w4a16_fused (route packing, FC1 + activation, FC2 + top-k
-sum) on one synthetic batch whose routing, activations and weights are already in HBM.
-Every step uses a fresh routing batch, so consecutive steps touch different experts the
-way consecutive decode steps do. The default workload is the decode shape: 128 experts,
-hidden 4096, intermediate 1536, top-8, NVFP4 weights, SiLU-SwiGLU, m = 8 tokens.
+A step is one call of moe_w4a16_fused (route packing, FC1 + activation, FC2 + top-k sum)
+on one synthetic batch whose routing, activations and weights are already in HBM. Steps
+rotate through distinct routing batches, so consecutive steps touch different experts the
+way consecutive decode steps do.
 
-Prints one JSON line: tokens/s of the whole layer, the effective weight bandwidth and
-TFLOP/s, the dominant kernel's roofline position (HIP events around each kernel, in a
-second pass of the same steps) and the CPU oracle's rate on a bounded sample.
+Timings of each workload and token count m:
+  cold      each call bracketed by its own HIP event pair, with a 512 MiB scratch write
+            before it (outside the timed region) so that neither the L2s nor the 256 MiB
+            Infinity Cache hold the previous call's weights; the median over the steps.
+  warm      the same calls back to back, one event pair around all of them (mean).
+  graph     the call captured once per routing batch into a HIP graph, the graphs replayed
+            back to back (mean): the warm, launch-overhead-free figure.
+  profiled  the measurement twin (moe_w4a16_fused_profiled) under the cold protocol: an
+            event after every kernel that launched, giving each kernel's mean duration.
+
+The JSON line's headline is the decode shape at m = 8 (128 experts, hidden 4096,
+intermediate 1536, top-8, NVFP4, SiLU-SwiGLU), cold. `sweep` holds decode m = 1 and 4 and
+the prefill shape at m = 2048 (256 experts, hidden 7168, intermediate 2048, top-8, NVFP4,
+Zipf-skewed routing), each with its own roofline; the prefill entry also carries the CPU
+oracle's rate on a bounded sample.
 """
 
 from __future__ import annotations
@@ -27,19 +38,23 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + effective weight GB/s (m=1..8) and TFLOP/s (m=2048), 1 GPU"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
-BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 / f16 MFMA
+SCRATCH_BYTES = 512 << 20       # cold protocol: written between calls
+PASSES = ("cold", "warm", "graph", "profiled")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200, help="timed steps of the headline (each pass)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "small", "prefill", "edge"])
-    ap.add_argument("--m", type=int, default=None, help="tokens per step (default: the workload's largest m)")
+    ap.add_argument("--m", type=int, default=None, help="tokens per step (default: decode 8, else the workload's largest m)")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "gemm"])
-    ap.add_argument("--sets", type=int, default=None, help="distinct routing batches rotated through")
-    ap.add_argument("--sweep", action="store_true", help="also report the workload's other token counts")
+    ap.add_argument("--passes", default=",".join(PASSES), help="comma-separated subset of " + ",".join(PASSES))
+    ap.add_argument("--no-sweep", action="store_true", help="headline only (no decode m = 1 / 4 and prefill entries)")
+    ap.add_argument("--sweep-steps", type=int, default=50, help="timed steps of each sweep entry (each pass)")
+    ap.add_argument("--sweep-warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--w4a8", action="store_true",
                     help="time the W4A8 variant (moe_w4a8_fused, MXFP4 workloads): whole-layer time only")
@@ -73,17 +88,17 @@ class HipEvents:
         if len(paths) != 1:
             raise RuntimeError(f"expected one HIP runtime in the process, found {paths}")
         self.hip = ctypes.CDLL(paths[0])
-        self.ev = (ctypes.c_void_p * n)()
-        for i in range(n):
+        self.ev = []
+        for _ in range(n):
             p = ctypes.c_void_p()
             rc = self.hip.hipEventCreate(ctypes.byref(p))
             if rc != 0:
                 raise RuntimeError(f"hipEventCreate failed ({rc})")
-            self.ev[i] = p
+            self.ev.append(p.value)
 
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()
-        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.ev[a]), ctypes.c_void_p(self.ev[b]))
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
         if rc != 0:
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return ms.value
@@ -111,8 +126,9 @@ def source_digest(*names):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel, workload, digest, per_launch_bytes):
-    """HBM traffic of the kernel from the committed rocprofv3 counter summary, if still current."""
+def load_traffic(kernel, workload, digest):
+    """HBM bytes per launch of the kernel from the committed rocprofv3 counter summary, if the
+    kernel's sources are unchanged since the counters were taken; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -123,43 +139,37 @@ def load_traffic(kernel, workload, digest, per_launch_bytes):
     return t.get("hbm_bytes_per_launch")
 
 
-def main():
-    args = parse()
-    if args.copy_probe:
-        copy_probe(args.copy_probe)
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              "(the layer has no multi-GPU path here).", file=sys.stderr)
-        sys.exit(2)
+class Layer:
+    """One workload's prepared weights (random canonical codes drawn on the GPU)."""
 
+    def __init__(self, moe, cfg, dev):
+        from synth import draw as D
+        self.moe, self.cfg, self.dev = moe, cfg, dev
+        self.codes = D.draw_random_codes_torch(cfg, seed=1000 + cfg.index, device=dev)
+        self.dims = moe.make_dims(cfg.fmt, cfg.act, cfg.num_experts, cfg.hidden, cfg.inter)
+        import torch
+        self.prepared_bytes = moe.moe_w4a16_prepared_size(self.dims)
+        self.prepared = torch.empty(self.prepared_bytes, dtype=torch.uint8, device=dev)
+        nv = cfg.fmt == "nvfp4"
+        c = self.codes
+        moe.moe_w4a16_prepare(self.dims, c["w13"], c["s13"], c["g13"] if nv else None, c["w2"], c["s2"],
+                              c["g2"] if nv else None, self.prepared, self.prepared_bytes)
+        torch.cuda.synchronize()
+
+
+def measure(layer, m, steps, warmup, args, passes):
+    """Time one (workload, m) under each requested pass; returns the JSON fields."""
     import numpy as np
     import torch
 
-    import fp4_weight_grouped_moe_amd as moe
-    from synth import configs as C
     from synth import draw as D
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    cfg = C.get_config(args.workload)
-    m = args.m or max(cfg.ms)
+    moe, cfg, dev = layer.moe, layer.cfg, layer.dev
     k, H = cfg.topk, cfg.hidden
     cap = moe.moe_route_pack_token_capacity(m)
-    total = args.steps + args.warmup
-    # rotate through distinct batches (bounded to ~256 MB of activations + routing)
-    sets = args.sets or min(total, max(1, int(256e6 // (m * H * 2 + m * k * 8))))
-    sets = max(1, min(sets, total))
+    total = steps + warmup
+    sets = min(total, max(1, int(256e6 // (m * H * 2 + m * k * 8))))
 
-    # weights: raw random code bytes drawn on the GPU, then prepared into the fragment layout
-    codes = D.draw_random_codes_torch(cfg, seed=1000 + cfg.index, device=dev)
-    layer = moe.MoeLayer(cfg.fmt, cfg.act, cfg.num_experts, H, cfg.inter, k, cap, device=dev)
-    nv = cfg.fmt == "nvfp4"
-    layer.prepare(codes["w13"], codes["s13"], codes["g13"] if nv else None, codes["w2"], codes["s2"],
-                  codes["g2"] if nv else None)
-    torch.cuda.synchronize()
-
-    # routing batches and activations
     ids_l, w_l, x_l, touched, valid = [], [], [], [], []
     emap = None
     for s in range(sets):
@@ -179,148 +189,268 @@ def main():
     d_x = torch.from_numpy(np.stack(x_l).view(np.int16)).to(dev).view(torch.bfloat16)
     d_map = torch.from_numpy(emap).to(dev) if emap is not None else None
     out = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
-    moe.moe_w4a16_set_path(args.path)
+    ws_bytes = moe.moe_w4a16_workspace_size(layer.dims, cap, k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    scratch = torch.empty(SCRATCH_BYTES, dtype=torch.uint8, device=dev)
 
-    # raw pointers resolved once so that the host launch rate does not limit small steps
+    # raw pointers resolved once, so that the host launch rate does not limit small steps
     lib = moe.lib()
     dims_ref = ctypes.byref(layer.dims)
-    stream = moe._stream(None)
-    ptrs = [(moe._ptr(d_x[s]), moe._ptr(d_ids[s]), moe._ptr(d_w[s])) for s in range(sets)]
-    fixed = (moe._ptr(layer.prepared), layer.prepared_bytes)
-    tail = (k, moe._ptr(d_map), cfg.num_global_experts, cap, moe._ptr(layer.workspace), layer.workspace_bytes,
-            moe._ptr(out), stream)
-
-    fused = lib.moe_w4a8_fused if args.w4a8 else (lib.moe_w4a16_fused_atomic_bf16 if args.atomic_bf16 else lib.moe_w4a16_fused)
+    ptrs = [(d_x[s].data_ptr(), d_ids[s].data_ptr(), d_w[s].data_ptr()) for s in range(sets)]
+    head = (layer.prepared.data_ptr(), layer.prepared_bytes)
+    tail = (k, d_map.data_ptr() if d_map is not None else None, cfg.num_global_experts, cap, ws.data_ptr(), ws_bytes,
+            out.data_ptr())
+    fused = lib.moe_w4a8_fused if args.w4a8 else (lib.moe_w4a16_fused_atomic_bf16 if args.atomic_bf16
+                                                  else lib.moe_w4a16_fused)
     whole_only = args.w4a8 or args.atomic_bf16      # the measurement twin runs the W4A16 layer
 
-    def step(i, events=None):
+    def call(i, stream=None):
         px, pi, pw = ptrs[i % sets]
-        if events is None:
-            rc = fused(dims_ref, fixed[0], fixed[1], px, m, pi, pw, *tail)
-        else:
-            arr = (ctypes.c_void_p * 5)(*events)
-            rc = lib.moe_w4a16_fused_profiled(dims_ref, fixed[0], fixed[1], px, m, pi, pw, *tail, arr, 5)
+        st = stream if stream is not None else torch.cuda.current_stream().cuda_stream
+        rc = fused(dims_ref, head[0], head[1], px, m, pi, pw, *tail, st)
         if rc != 0:
-            raise moe.MoeError(rc, "moe_w4a16_fused", moe.moe_last_error())
+            raise moe.MoeError(rc, "fused call", moe.moe_last_error())
 
-    # ---- pass A: whole-layer throughput
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    e1.record()
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    def cold_fill(i):
+        scratch.fill_(i & 0xFF)
 
-    # ---- pass B: per-kernel durations from events between the launches, same steps (the
-    # measurement twin runs the W4A16 layer, so the W4A8 line reports the whole layer only)
-    names = ["route_pack", "fc1", "fc2", "combine"]
-    per = {n: 0.0 for n in names}
-    if not whole_only:
-        hev = HipEvents(5 * args.steps)
-        for i in range(args.steps):
-            step(args.warmup + i, [hev.ev[5 * i + j] for j in range(5)])
+    res = {"m": m, "token_capacity": cap, "routing_sets": sets}
+    stream = torch.cuda.current_stream().cuda_stream
+    moe.moe_w4a16_set_path(args.path)
+    try:
+        for i in range(warmup):
+            cold_fill(i)
+            call(i, stream)
         torch.cuda.synchronize()
-        for i in range(args.steps):
-            for j, n in enumerate(names):
-                per[n] += hev.elapsed_ms(5 * i + j, 5 * i + j + 1)
-        per = {n: v / args.steps for n, v in per.items()}
-    moe.moe_w4a16_set_path("auto")
 
-    used = [(args.warmup + i) % sets for i in range(args.steps)]
+        if "cold" in passes:
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            torch.cuda.synchronize()
+            for i in range(steps):
+                cold_fill(warmup + i)
+                ev[i][0].record()
+                call(warmup + i, stream)
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            t = np.array([a.elapsed_time(b) for a, b in ev])
+            res["cold"] = {"ms_median": round(float(np.median(t)), 5), "ms_p10": round(float(np.percentile(t, 10)), 5),
+                           "ms_p90": round(float(np.percentile(t, 90)), 5), "samples": steps}
+
+        if "warm" in passes:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(steps):
+                call(warmup + i, stream)
+            e1.record()
+            torch.cuda.synchronize()
+            res["warm"] = {"ms_mean": round(e0.elapsed_time(e1) / steps, 5), "samples": steps,
+                           "note": "back to back, rotating routing batches"}
+
+        if "graph" in passes:
+            n_graphs = min(sets, 8)
+            graphs = []
+            for gi in range(n_graphs):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    call(gi)                     # the capture stream is torch's current stream here
+                graphs.append(g)
+            for g in graphs:
+                g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(steps):
+                graphs[i % n_graphs].replay()
+            e1.record()
+            torch.cuda.synchronize()
+            res["graph"] = {"ms_mean": round(e0.elapsed_time(e1) / steps, 5), "samples": steps,
+                            "note": f"HIP graph replay back to back, {n_graphs} routing batches"}
+            del graphs
+
+        per = {}
+        if "profiled" in passes and not whole_only:
+            hev = HipEvents(6 * steps)
+            names = []
+            for i in range(steps):
+                cold_fill(warmup + i)
+                px, pi, pw = ptrs[(warmup + i) % sets]
+                evs = (ctypes.c_void_p * 6)(*hev.ev[6 * i:6 * i + 6])
+                kid = (ctypes.c_int32 * 5)()
+                n = ctypes.c_int(0)
+                rc = lib.moe_w4a16_fused_profiled(dims_ref, head[0], head[1], px, m, pi, pw, *tail, stream, evs, 6,
+                                                  kid, ctypes.byref(n))
+                if rc != 0:
+                    raise moe.MoeError(rc, "moe_w4a16_fused_profiled", moe.moe_last_error())
+                names.append([moe.KERNEL_NAMES[kid[j]] for j in range(n.value)])
+            torch.cuda.synchronize()
+            for i in range(steps):
+                for j, name in enumerate(names[i]):
+                    per.setdefault(name, []).append(hev.elapsed_ms(hev.ev[6 * i + j], hev.ev[6 * i + j + 1]))
+            res["kernel_us"] = {n: round(float(np.mean(v)) * 1e3, 2) for n, v in per.items()}
+            res["kernels_launched"] = names[0]
+            del hev
+    finally:
+        moe.moe_w4a16_set_path("auto")
+
+    used = [(warmup + i) % sets for i in range(steps)]
     avg_touched = float(np.mean([touched[s] for s in used]))
     avg_valid = float(np.mean([valid[s] for s in used]))
     w13b, w2b = expert_bytes(cfg)
     weight_bytes = avg_touched * (w13b + w2b)
-    step_bytes = weight_bytes + 2 * m * H * 2
     flops = avg_valid * 2.0 * (H * cfg.n1 + cfg.inter * H)
-    t = ms_per_step * 1e-3
-    decode_path = args.path == "decode" or (args.path == "auto" and m <= moe.MOE_DECODE_MAX_M and cap <= moe.MOE_DECODE_MAX_M)
-    kernel_src = "decode.hip" if decode_path else "gemm.hip"
-    if whole_only:
-        roof = None
-    elif decode_path:
-        # dominant kernel: FC1 (W13 is two thirds of the streamed weights)
-        dom = "fc1"
-        dom_bytes = avg_touched * w13b + m * H * 2 + avg_valid * cfg.inter * 2
-        achieved = dom_bytes / (per[dom] * 1e-3) / 1e9
-        traffic = load_traffic("decode_fc1", args.workload + f"_m{m}", source_digest(kernel_src, "device.hpp"), dom_bytes)
-        roof = {"bound": "hbm", "kernel": "decode_fc1_kernel", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "algorithmic_bytes_per_launch": int(dom_bytes),
-                "avg_launch_us": round(per[dom] * 1e3, 2)}
-    else:
-        dom = "fc1" if per["fc1"] >= per["fc2"] else "fc2"
-        dom_flops = avg_valid * 2.0 * (H * cfg.n1 if dom == "fc1" else cfg.inter * H)
-        achieved = dom_flops / (per[dom] * 1e-3) / 1e12
-        traffic = load_traffic(f"gemm_{dom}", args.workload + f"_m{m}", source_digest(kernel_src, "device.hpp"), None)
-        roof = {"bound": "mfma", "kernel": f"gemm_kernel<{dom}>", "achieved": round(achieved, 1),
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic, "algorithmic_flops_per_launch": int(dom_flops),
-                "avg_launch_us": round(per[dom] * 1e3, 2)}
+    res.update({"touched_experts_avg": round(avg_touched, 2), "valid_routes_avg": round(avg_valid, 2),
+                "weight_bytes_per_step": int(weight_bytes), "layer_bytes_per_step": int(weight_bytes + 2 * m * H * 2),
+                "useful_flops_per_step": int(flops)})
+    for key in ("cold", "warm", "graph"):
+        if key in res:
+            t = (res[key].get("ms_median") or res[key]["ms_mean"]) * 1e-3
+            res[key].update({"tokens_per_s": round(m / t, 1), "weight_GBps": round(weight_bytes / t / 1e9, 1),
+                             "hbm_frac": round(weight_bytes / t / 1e9 / HBM_PEAK_GBPS, 4),
+                             "tflops": round(flops / t / 1e12, 3),
+                             "mfma_frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 5)})
 
+    if per:
+        decode_path = "combine" not in per           # the decode path has no combine pass
+    else:
+        decode_path = args.path == "decode" or (args.path == "auto" and m <= moe.MOE_DECODE_MAX_M
+                                                and cap <= moe.MOE_DECODE_MAX_M)
+    res["path"] = "decode" if decode_path else "gemm"
+    kernel_src = "decode.hip" if decode_path else "gemm.hip"
+    workload_tag = f"{cfg.name}_m{m}"
+    if not per:
+        res["roofline"] = None
+    elif decode_path:
+        # dominant kernel: FC1 (W13 is two thirds of the streamed weights); algorithmic bytes
+        # per launch = the touched experts' W13 codes + scales + globals, the activation rows
+        # read and the intermediate rows written
+        dom_bytes = avg_touched * w13b + m * H * 2 + avg_valid * cfg.inter * 2
+        achieved = dom_bytes / (np.mean(per["fc1"]) * 1e-3) / 1e9
+        res["roofline"] = {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic("decode_fc1", workload_tag, source_digest(kernel_src, "device.hpp")),
+            "kernel": "decode_fc1_kernel", "algorithmic_bytes_per_launch": int(dom_bytes),
+            "avg_launch_us": round(float(np.mean(per["fc1"])) * 1e3, 2)}
+    else:
+        dom = "fc1" if np.mean(per["fc1"]) >= np.mean(per["fc2"]) else "fc2"
+        dom_flops = avg_valid * 2.0 * (H * cfg.n1 if dom == "fc1" else cfg.inter * H)
+        achieved = dom_flops / (np.mean(per[dom]) * 1e-3) / 1e12
+        res["roofline"] = {
+            "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": load_traffic(f"gemm_{dom}", workload_tag, source_digest(kernel_src, "device.hpp")),
+            "kernel": f"gemm_kernel<{dom}>", "algorithmic_flops_per_launch": int(dom_flops),
+            "avg_launch_us": round(float(np.mean(per[dom])) * 1e3, 2)}
+    res["workload"] = (f"{cfg.name}: E{cfg.num_experts} H{H} I{cfg.inter} top{k} {cfg.fmt.upper()} {cfg.act} m={m}")
+    res["_batches"] = (ids_l, w_l, x_l, emap)
+    del d_ids, d_w, d_x, out, ws, scratch
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer has no multi-GPU path here).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp4_weight_grouped_moe_amd as moe
+    from synth import configs as C
+
+    passes = tuple(p for p in args.passes.split(",") if p)
+    bad = [p for p in passes if p not in PASSES]
+    if bad:
+        raise SystemExit(f"unknown passes {bad}")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = C.get_config(args.workload)
+    m = args.m or (8 if args.workload == "decode" else max(cfg.ms))
+
+    layer = Layer(moe, cfg, dev)
+    head = measure(layer, m, args.steps, args.warmup, args, passes)
+    batches = head.pop("_batches")
+    key = "cold" if "cold" in head else ("warm" if "warm" in head else "graph")
+    if key not in head:
+        raise SystemExit("the headline needs at least one of the cold, warm or graph passes")
+    ms = head[key].get("ms_median") or head[key]["ms_mean"]
     res = {
         "metric": METRIC,
-        "value": round(m / t, 1),
+        "value": round(m / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: E{cfg.num_experts} H{H} I{cfg.inter} top{k} {cfg.fmt.upper()} "
-                               f"{cfg.act} m={m}", "m": m, "token_capacity": cap, "routing_sets": sets,
-                   "path": "decode" if decode_path else "gemm", "variant": "w4a8" if args.w4a8 else ("w4a16-atomic-bf16" if args.atomic_bf16 else "w4a16")},
-        "effective_weight_GBps": round(weight_bytes / t / 1e9, 1),
-        "weight_hbm_frac": round(weight_bytes / t / 1e9 / HBM_PEAK_GBPS, 4),
-        "layer_bytes_per_step": int(step_bytes),
-        "tflops": round(flops / t / 1e12, 3),
-        "mfma_frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 5),
-        "touched_experts_avg": round(avg_touched, 2),
-        "kernel_us": None if whole_only else {n: round(v * 1e3, 2) for n, v in per.items()},
-        "roofline": roof,
+        "config": {"workload": head["workload"], "m": m, "token_capacity": head["token_capacity"],
+                   "routing_sets": head["routing_sets"], "path": head["path"], "timing": key,
+                   "variant": "w4a8" if args.w4a8 else ("w4a16-atomic-bf16" if args.atomic_bf16 else "w4a16")},
+        "effective_weight_GBps": head[key]["weight_GBps"],
+        "weight_hbm_frac": head[key]["hbm_frac"],
+        "tflops": head[key]["tflops"],
+        "mfma_frac": head[key]["mfma_frac"],
+        "touched_experts_avg": head["touched_experts_avg"],
+        "cold": head.get("cold"), "warm": head.get("warm"), "graph": head.get("graph"),
+        "kernel_us": head.get("kernel_us"),
+        "roofline": head.get("roofline"),
     }
-    del codes
-    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline and not (args.w4a8 or args.atomic_bf16):
+        res["cpu_baseline"] = cpu_baseline(layer, m, batches, args.cpu_seconds)
 
-    if not args.no_cpu_baseline and not whole_only:
-        res["cpu_baseline"] = cpu_baseline(cfg, ids_l, w_l, x_l, emap, dev, m, args.cpu_seconds)
+    if not args.no_sweep and args.workload == "decode" and m == 8 and not (args.w4a8 or args.atomic_bf16):
+        sweep = []
+        for mm in (1, 4):
+            r = measure(layer, mm, args.sweep_steps, args.sweep_warmup, args, passes)
+            r.pop("_batches")
+            sweep.append(r)
+        del layer
+        torch.cuda.empty_cache()
+        pre = Layer(moe, C.get_config("prefill"), dev)
+        r = measure(pre, 2048, args.sweep_steps, args.sweep_warmup, args, passes)
+        b = r.pop("_batches")
+        if not args.no_cpu_baseline:
+            r["cpu_baseline"] = cpu_baseline(pre, 2048, b, args.cpu_seconds)
+        sweep.append(r)
+        res["sweep"] = sweep
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(cfg, ids_l, w_l, x_l, emap, dev, m, target_s):
-    """The CPU oracle on the workload's routing batches in turn (same codes, regenerated on the
-    GPU) until about target_s seconds of oracle time: whole batches while one batch takes less
-    than the target, else a prefix of the first batch's tokens."""
+def cpu_baseline(layer, m, batches, target_s):
+    """The CPU oracle on the workload's routing batches in turn (the same codes, copied back
+    from the device) until about target_s seconds of oracle time: whole batches while one batch
+    takes less than the target, else a prefix of the first batch's tokens."""
     import numpy as np
-    import torch
 
     from oracle import formats as F
     from oracle import moe as M
     from oracle.route_pack import local_ids
-    from synth import draw as D
 
+    cfg = layer.cfg
+    ids_l, w_l, x_l, emap = batches
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    codes = D.draw_random_codes_torch(cfg, seed=1000 + cfg.index, device=dev)
 
     def run(b, n):
         ids, w, x = ids_l[b], w_l[b], F.bf16_bits_to_f64(x_l[b])
         lid = local_ids(ids, emap, cfg.num_global_experts, cfg.num_experts).reshape(m, cfg.topk)
         toks = np.arange(n)
         need = sorted(int(e) for e in np.unique(lid[toks][lid[toks] >= 0]))
-        host = {key: codes[key][need].cpu().numpy() for key in ("w13", "s13", "w2", "s2", "g13", "g2")}
-        ex = M.Experts(cfg.fmt, cfg.act, cfg.hidden, cfg.inter, host, expert_ids=need)
+        host = {key: layer.codes[key][need].cpu().numpy() for key in ("w13", "s13", "w2", "s2", "g13", "g2")}
+        ex = M.Experts(cfg.fmt, cfg.act, cfg.hidden, cfg.inter, host, expert_ids=need, cache=False)
         t0 = time.perf_counter()
         M.moe_forward(x, ids, w, emap, cfg.num_global_experts, cfg.num_experts, ex, tokens=toks)
         return time.perf_counter() - t0
@@ -332,15 +462,13 @@ def cpu_baseline(cfg, ids_l, w_l, x_l, emap, dev, m, target_s):
         if elapsed >= target_s or n >= m:
             break
         n = min(m, max(n + 1, int(np.ceil(n * target_s / max(elapsed, 1e-3)))))
-    tokens, batches = n, 1
+    tokens, nb = n, 1
     # whole batches are short: add the next routing batches up to the target
-    while n == m and elapsed < target_s and batches < len(ids_l):
-        elapsed += run(batches, m)
+    while n == m and elapsed < target_s and nb < len(ids_l):
+        elapsed += run(nb, m)
         tokens += m
-        batches += 1
-    del codes
-    torch.cuda.empty_cache()
-    sample = (f"{batches} routing batches of {m} tokens" if batches > 1 else f"first {n} of {m} tokens of one batch")
+        nb += 1
+    sample = (f"{nb} routing batches of {m} tokens" if nb > 1 else f"first {n} of {m} tokens of one batch")
     return {"value": round(tokens / elapsed, 4), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{sample} ({cfg.topk} routes each), float64 NumPy, dequantisation of the touched "
                       f"experts included; {elapsed:.1f} s"}

@@ -82,7 +82,8 @@ def _load():
         "moe_w4a16_fused": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
         "moe_w4a8_fused": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
         "moe_w4a16_fused_atomic_bf16": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
-        "moe_w4a16_fused_profiled": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P, P, I32]),
+        "moe_w4a16_fused_profiled": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P, P, I32,
+                                           ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int)]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_w4a16_set_path": (I32, [I32]),
         "moe_w4a16_set_decode_max_m": (I32, [I32]),
@@ -129,6 +130,46 @@ def _check(rc: int, where: str) -> int:
     if rc < 0:
         raise MoeError(rc, where, moe_last_error())
     return rc
+
+
+def _require(t, name: str, dtype, rows, cols, device, where: str) -> None:
+    """Raise MoeError (MOE_ERR_INVALID_ARG) unless torch tensor ``t`` has this dtype, is contiguous
+    and holds at least ``rows`` rows of ``cols`` elements ([rows, cols], or [rows] when cols is
+    None); _require_device then checks that every tensor sits on the same GPU. Raw integer pointers and None pass
+    unchecked: they are the caller's responsibility. No arithmetic: a mismatch here (int64 ids,
+    a transposed view, a host tensor) would otherwise be read as wrong data without an error."""
+    if t is None or isinstance(t, int):
+        return
+    if t.dtype != dtype:
+        raise MoeError(MOE_ERR_INVALID_ARG, where, f"{name} must be {dtype}, got {t.dtype}")
+    shape = tuple(t.shape)
+    ok = (len(shape) == 1 and shape[0] >= rows) if cols is None else (len(shape) == 2 and shape[0] >= rows
+                                                                       and shape[1] == cols)
+    if not ok:
+        want = f"[>= {rows}]" if cols is None else f"[>= {rows}, {cols}]"
+        raise MoeError(MOE_ERR_INVALID_ARG, where, f"{name} must have shape {want}, got {list(shape)}")
+    if not t.is_contiguous():
+        raise MoeError(MOE_ERR_INVALID_ARG, where, f"{name} must be contiguous")
+
+
+def _require_device(t, name: str, device, where: str) -> None:
+    if t is None or isinstance(t, int):
+        return
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise MoeError(MOE_ERR_INVALID_ARG, where, f"{name} is on {t.device}, expected {device or 'a GPU'}")
+
+
+def _check_fused_args(dims, x, m, topk_ids, topk_weights, topk, expert_map, num_global_experts, out, where) -> None:
+    import torch
+    args = (("x", x, torch.bfloat16, m, dims.hidden), ("topk_ids", topk_ids, torch.int32, m, topk),
+            ("topk_weights", topk_weights, torch.float32, m, topk),
+            ("expert_map", expert_map, torch.int32, num_global_experts, None),
+            ("out", out, torch.bfloat16, m, dims.hidden))
+    for name, t, dtype, rows, cols in args:
+        _require(t, name, dtype, rows, cols, None, where)
+    device = next((t.device for _, t, *_ in args if t is not None and not isinstance(t, int)), None)
+    for name, t, *_ in args:
+        _require_device(t, name, device, where)
 
 
 def make_dims(fmt, act, num_experts: int, hidden: int, inter: int) -> moe_w4a16_dims:
@@ -184,6 +225,7 @@ def moe_w4a16_workspace_size(dims: moe_w4a16_dims, token_capacity: int, topk: in
 def moe_w4a16_fused(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: int, topk_ids, topk_weights,
                     topk: int, expert_map, num_global_experts: int, token_capacity: int, workspace,
                     workspace_bytes: int, out, stream=None) -> None:
+    _check_fused_args(dims, x, m, topk_ids, topk_weights, topk, expert_map, num_global_experts, out, "moe_w4a16_fused")
     _check(_lib.moe_w4a16_fused(ctypes.byref(dims), _ptr(prepared), prepared_bytes, _ptr(x), m, _ptr(topk_ids),
                                 _ptr(topk_weights), topk, _ptr(expert_map), num_global_experts, token_capacity,
                                 _ptr(workspace), workspace_bytes, _ptr(out), _stream(stream)), "moe_w4a16_fused")
@@ -192,6 +234,7 @@ def moe_w4a16_fused(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: i
 def moe_w4a8_fused(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: int, topk_ids, topk_weights,
                    topk: int, expert_map, num_global_experts: int, token_capacity: int, workspace,
                    workspace_bytes: int, out, stream=None) -> None:
+    _check_fused_args(dims, x, m, topk_ids, topk_weights, topk, expert_map, num_global_experts, out, "moe_w4a8_fused")
     _check(_lib.moe_w4a8_fused(ctypes.byref(dims), _ptr(prepared), prepared_bytes, _ptr(x), m, _ptr(topk_ids),
                                _ptr(topk_weights), topk, _ptr(expert_map), num_global_experts, token_capacity,
                                _ptr(workspace), workspace_bytes, _ptr(out), _stream(stream)), "moe_w4a8_fused")
@@ -200,21 +243,32 @@ def moe_w4a8_fused(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: in
 def moe_w4a16_fused_atomic_bf16(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: int, topk_ids,
                                 topk_weights, topk: int, expert_map, num_global_experts: int, token_capacity: int,
                                 workspace, workspace_bytes: int, out, stream=None) -> None:
+    _check_fused_args(dims, x, m, topk_ids, topk_weights, topk, expert_map, num_global_experts, out, "moe_w4a16_fused_atomic_bf16")
     _check(_lib.moe_w4a16_fused_atomic_bf16(ctypes.byref(dims), _ptr(prepared), prepared_bytes, _ptr(x), m,
                                             _ptr(topk_ids), _ptr(topk_weights), topk, _ptr(expert_map),
                                             num_global_experts, token_capacity, _ptr(workspace), workspace_bytes,
                                             _ptr(out), _stream(stream)), "moe_w4a16_fused_atomic_bf16")
 
 
+KERNEL_NAMES = ("route_pack", "fc1", "requant", "fc2", "combine")    # moe_kernel_id order
+
+
 def moe_w4a16_fused_profiled(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: int, topk_ids, topk_weights,
                              topk: int, expert_map, num_global_experts: int, token_capacity: int, workspace,
-                             workspace_bytes: int, out, events, stream=None) -> None:
-    """``events``: five or more torch.cuda.Event(enable_timing=True); their HIP handles are passed down."""
-    arr = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
+                             workspace_bytes: int, out, events, stream=None):
+    """``events``: six or more HIP event handles (ints) or torch.cuda.Event(enable_timing=True).
+    Returns the names of the kernels launched, in order; event j + 1 follows kernel j."""
+    _check_fused_args(dims, x, m, topk_ids, topk_weights, topk, expert_map, num_global_experts, out,
+                      "moe_w4a16_fused_profiled")
+    arr = (ctypes.c_void_p * len(events))(*[e if isinstance(e, int) else int(e.cuda_event) for e in events])
+    ids = (ctypes.c_int32 * 5)()
+    n = ctypes.c_int(0)
     _check(_lib.moe_w4a16_fused_profiled(ctypes.byref(dims), _ptr(prepared), prepared_bytes, _ptr(x), m,
                                          _ptr(topk_ids), _ptr(topk_weights), topk, _ptr(expert_map),
                                          num_global_experts, token_capacity, _ptr(workspace), workspace_bytes,
-                                         _ptr(out), _stream(stream), arr, len(events)), "moe_w4a16_fused_profiled")
+                                         _ptr(out), _stream(stream), arr, len(events), ids, ctypes.byref(n)),
+           "moe_w4a16_fused_profiled")
+    return [KERNEL_NAMES[ids[i]] for i in range(n.value)]
 
 
 def moe_w4a16_prepare_layout(dims: moe_w4a16_dims, layout: moe_w4a16_source_layout, w13, s13, g13, w2, s2, g2,

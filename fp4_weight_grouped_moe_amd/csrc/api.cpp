@@ -251,7 +251,7 @@ namespace {
 int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes, const uint16_t* x, int64_t m,
                const int32_t* topk_ids, const float* topk_weights, int topk, const int32_t* expert_map,
                int num_global_experts, int64_t token_capacity, void* workspace, size_t workspace_bytes, uint16_t* out,
-               hipStream_t stream, hipEvent_t* events, bool w4a8 = false, bool atomic_bf16 = false) {
+               hipStream_t stream, LaunchMarks* marks, bool w4a8 = false, bool atomic_bf16 = false) {
   if (int rc = check_dims(dims)) return rc;
   if (w4a8 && dims->fmt != MOE_FMT_MXFP4_E8M0_K32)
     return fail(MOE_ERR_UNSUPPORTED, "the W4A8 variant needs MXFP4 weights (E8M0 block scales)");
@@ -360,15 +360,14 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
     fp.num_global_experts = num_global_experts;
   }
 
-  if (events) (void)hipEventRecord(events[0], stream);
+  if (marks) (void)hipEventRecord(marks->events[0], stream);
   // extra route-pack workgroups for the conversion: one wave per row, 16 waves each
   const int side_blocks = decode ? int((m + 15) / 16) : cus;
   if (!fc1_packs) {
     if (hipError_t e = launch_route_pack(rp, side_blocks, stream); e != hipSuccess)
       return launch_status(e, "route pack launch");
+    if (marks) marks->after(stream, KID_ROUTE_PACK);
   }
-  if (events) (void)hipEventRecord(events[1], stream);
-  hipEvent_t* marks = events ? events + 2 : nullptr;
   hipError_t e = decode ? launch_decode(fp, cus, stream, marks) : launch_gemm(fp, cus, stream, marks);
   return launch_status(e, decode ? "decode launch" : "grouped GEMM launch");
 }
@@ -405,10 +404,16 @@ int moe_w4a16_fused_profiled(const moe_w4a16_dims* dims, const void* prepared, s
                              const uint16_t* x, int64_t m, const int32_t* topk_ids, const float* topk_weights,
                              int topk, const int32_t* expert_map, int num_global_experts, int64_t token_capacity,
                              void* workspace, size_t workspace_bytes, uint16_t* out, hipStream_t stream,
-                             hipEvent_t* events, int num_events) {
-  if (!events || num_events < 5) return fail(MOE_ERR_INVALID_ARG, "events must hold at least 5 HIP events");
-  return fused_impl(dims, prepared, prepared_bytes, x, m, topk_ids, topk_weights, topk, expert_map,
-                    num_global_experts, token_capacity, workspace, workspace_bytes, out, stream, events);
+                             hipEvent_t* events, int num_events, int32_t* kernel_ids, int* num_kernels) {
+  if (!events || num_events < kMaxMarks + 1)
+    return fail(MOE_ERR_INVALID_ARG, "events must hold at least %d HIP events", kMaxMarks + 1);
+  if (!kernel_ids || !num_kernels) return fail(MOE_ERR_INVALID_ARG, "kernel_ids and num_kernels must be non-NULL");
+  LaunchMarks marks{events, kernel_ids, 0};
+  *num_kernels = 0;
+  const int rc = fused_impl(dims, prepared, prepared_bytes, x, m, topk_ids, topk_weights, topk, expert_map,
+                            num_global_experts, token_capacity, workspace, workspace_bytes, out, stream, &marks);
+  *num_kernels = marks.n;
+  return rc;
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }

@@ -825,7 +825,7 @@ hipError_t allow_lds(K kernel, int bytes) {
 }
 
 template <int FMT>
-hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t stream, hipEvent_t* marks) {
+hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t stream, LaunchMarks* marks) {
   static const hipError_t lds_ok = [] {
     // dynamic LDS: FC1 staged rows + exponents (+ pack tables); FC2 block table + slot tokens
     hipError_t e = allow_lds(&decode_fc1_kernel<FMT, true, false>, kDecodeStageBytes + 256);
@@ -850,7 +850,7 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
     hipLaunchKernelGGL((decode_fc1_kernel<FMT, true, false>), dim3(grid1), dim3(kF1Threads), lds1, stream, p);
   else
     hipLaunchKernelGGL((decode_fc1_kernel<FMT, false, false>), dim3(grid1), dim3(kF1Threads), 0, stream, p);
-  if (marks) (void)hipEventRecord(marks[0], stream);
+  if (marks) marks->after(stream, KID_FC1);
   constexpr int RG = kF3RowGroups;
   const size_t lds3 = f3_lds_bytes<RG>(p.m, p.topk, p.cap_blocks);
   // (the intermediate rows are addressed through a buffer resource: 32-bit offsets)
@@ -860,8 +860,10 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
   // FC2 multiplies their exact values in bf16
   const bool w8 = FMT == FMT_MXFP4 && p.w4a8 && p.inter8 != nullptr && split &&
                   f8_lds_bytes<RG>(p.m, p.topk, p.cap_blocks) <= size_t(kF3MaxLds);
-  if (p.w4a8)
+  if (p.w4a8) {
     if (hipError_t e = launch_mxfp8_requant(p, w8, stream); e != hipSuccess) return e;
+    if (marks) marks->after(stream, KID_REQUANT);
+  }
   if (split) {
     const int nsplit = int((g.kb2 + kF3KB - 1) / kF3KB);
     const int64_t pairs = ((g.n2_groups + RG - 1) / RG) * ((nsplit + 1) / 2);
@@ -870,17 +872,11 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
                          f8_lds_bytes<RG>(p.m, p.topk, p.cap_blocks), stream, p);
     else
       hipLaunchKernelGGL((decode_fc2_split_kernel<FMT, RG, false>), dim3((pairs + 7) / 8 * 16), dim3(kF3Threads), lds3, stream, p);
-    if (marks) {
-      (void)hipEventRecord(marks[1], stream);
-      (void)hipEventRecord(marks[2], stream);
-    }
+    if (marks) marks->after(stream, KID_FC2);
   } else {
     const size_t lds2 = size_t(p.cap_blocks) * 4 + size_t(p.cap_blocks) * kBlockM * 4;
     hipLaunchKernelGGL((decode_fc2_kernel<FMT>), dim3(g.n2_groups), dim3(kF2Threads), lds2, stream, p);
-    if (marks) {
-      (void)hipEventRecord(marks[1], stream);
-      (void)hipEventRecord(marks[2], stream);
-    }
+    if (marks) marks->after(stream, KID_FC2);
   }
   return hipGetLastError();
 }
@@ -897,7 +893,7 @@ bool decode_fc1_packs(const PreparedGeom& g, int64_t m, int topk) {
              size_t(kLdsPerCU);
 }
 
-hipError_t launch_decode(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks) {
+hipError_t launch_decode(const FusedParams& p, int num_cus, hipStream_t stream, LaunchMarks* marks) {
   return p.g.fmt == FMT_NVFP4 ? launch_decode_fmt<FMT_NVFP4>(p, num_cus, stream, marks)
                               : launch_decode_fmt<FMT_MXFP4>(p, num_cus, stream, marks);
 }

@@ -463,7 +463,7 @@ hipError_t allow_large_lds(size_t lds) {
   return once;
 }
 
-hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks) {
+hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, LaunchMarks* marks) {
   // One 8-wave workgroup per CU (two waves per SIMD, up to 256 registers each).
   const int grid = num_cus;
   const size_t lds = kLdsBytes;
@@ -473,14 +473,18 @@ hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hi
   const bool nv = p.g.fmt == FMT_NVFP4;
   if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 1>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 1>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
-  if (marks) (void)hipEventRecord(marks[0], stream);
-  if (p.w4a8)
+  if (marks) marks->after(stream, KID_FC1);
+  if (p.w4a8) {
     if (hipError_t e2 = launch_mxfp8_requant(p, false, stream); e2 != hipSuccess) return e2;
+    if (marks) marks->after(stream, KID_REQUANT);
+  }
   if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
-  if (marks) (void)hipEventRecord(marks[1], stream);
-  if (!p.atomic_bf16) launch_combine(p, stream);
-  if (marks) (void)hipEventRecord(marks[2], stream);
+  if (marks) marks->after(stream, KID_FC2);
+  if (!p.atomic_bf16) {
+    launch_combine(p, stream);
+    if (marks) marks->after(stream, KID_COMBINE);
+  }
   return hipGetLastError();
 }
 

@@ -108,13 +108,26 @@ size_t route_pack_lds_bytes(int num_experts, int64_t num_routes, int64_t cap_rou
 // `side_blocks` extra workgroups do the activation conversion when p.x16 is set.
 hipError_t launch_route_pack(const RoutePackParams& p, int side_blocks, hipStream_t stream);
 hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream);
-// `marks` (nullable) receives an event record after each kernel: FC1, FC2, then the top-k
-// combine (the decode path records its last mark right after FC2).
-hipError_t launch_decode(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks);
+// Measurement marks: after each kernel a launcher enqueues, one event record on the same
+// stream and the kernel's id (MOE_KERNEL_* of the C ABI) -- only for kernels that launched.
+struct LaunchMarks {
+  hipEvent_t* events;            // events[0] is recorded before the first launch
+  int32_t* ids;
+  int n;
+  void after(hipStream_t stream, int id) {
+    (void)hipEventRecord(events[n + 1], stream);
+    ids[n++] = id;
+  }
+};
+enum KernelId : int32_t { KID_ROUTE_PACK = 0, KID_FC1 = 1, KID_REQUANT = 2, KID_FC2 = 3, KID_COMBINE = 4 };
+constexpr int kMaxMarks = 5;
+
+// `marks` (nullable) receives a mark after each kernel launched.
+hipError_t launch_decode(const FusedParams& p, int num_cus, hipStream_t stream, LaunchMarks* marks);
 // True when the decode FC1 launch packs the routes itself for these sizes (the fused call then
 // launches no route pack); false for the grouped-GEMM path.
 bool decode_fc1_packs(const PreparedGeom& g, int64_t m, int topk);
-hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, hipEvent_t* marks);
+hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, LaunchMarks* marks);
 // out = bf16 of the sum of each token's valid route rows y[route] (route order).
 void launch_combine(const FusedParams& p, hipStream_t stream);
 // W4A8: every valid intermediate row rounded to MXFP8 (between FC1 and FC2): as the exact

@@ -471,12 +471,14 @@ __global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParam
       amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(v[i] << 16)), fabsf(__uint_as_float(v[i] & 0xFFFF0000u))));
     return amax;
   };
-  auto to_f16 = [](const u32x4 v, float inv) {
+  // Each value times 2^-pexp by ldexp: a row whose maximum is below 2^-113 has pexp <= -128,
+  // where the factor 2^-pexp alone would overflow to +inf.
+  auto to_f16 = [](const u32x4 v, int pexp) {
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const _Float16 lo = (_Float16)(__uint_as_float(v[i] << 16) * inv);
-      const _Float16 hi = (_Float16)(__uint_as_float(v[i] & 0xFFFF0000u) * inv);
+      const _Float16 lo = (_Float16)ldexpf(__uint_as_float(v[i] << 16), -pexp);
+      const _Float16 hi = (_Float16)ldexpf(__uint_as_float(v[i] & 0xFFFF0000u), -pexp);
       o[i] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
     }
     return o;
@@ -501,11 +503,10 @@ __global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParam
       for (int i = 0; i < kRowRegs; ++i) amax = chunk_max(w[i], amax);
     }
     const int pexp = pexp_of(row_max(amax));
-    const float inv = ldexpf(1.f, -pexp);
     if (chunks <= 64 * kRowRegs) {
 #pragma unroll
       for (int i = 0; i < kRowRegs; ++i)
-        if (lane + 64 * i < chunks) __builtin_amdgcn_raw_buffer_store_b128(to_f16(v[i], inv), dst, (lane + 64 * i) * 16, 0, 0);
+        if (lane + 64 * i < chunks) __builtin_amdgcn_raw_buffer_store_b128(to_f16(v[i], pexp), dst, (lane + 64 * i) * 16, 0, 0);
     } else {
       for (int base = 0; base < chunks; base += 64 * kRowRegs) {
         u32x4 w[kRowRegs];
@@ -513,7 +514,7 @@ __global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParam
         for (int i = 0; i < kRowRegs; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b128(src, (base + lane + 64 * i) * 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < kRowRegs; ++i)
-          if (base + lane + 64 * i < chunks) __builtin_amdgcn_raw_buffer_store_b128(to_f16(w[i], inv), dst, (base + lane + 64 * i) * 16, 0, 0);
+          if (base + lane + 64 * i < chunks) __builtin_amdgcn_raw_buffer_store_b128(to_f16(w[i], pexp), dst, (base + lane + 64 * i) * 16, 0, 0);
       }
     }
     if (lane == 0) p.xexp[t] = pexp;

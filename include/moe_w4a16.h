@@ -227,16 +227,30 @@ int moe_w4a16_fused_atomic_bf16(const moe_w4a16_dims* dims, const void* prepared
 
 /* ------------------------------------------------------------------ diagnostics */
 
-/* Measurement twin of moe_w4a16_fused: the same launches on `stream`, with HIP event
- * records between them -- events[0] before route packing, [1] after it, [2] after FC1,
- * [3] after FC2, [4] after the top-k combine (decode path: [4] right after [3]). The
- * caller creates the events (num_events >= 5). Not for graph capture. */
+/* Measurement twin of moe_w4a16_fused: the same launches on `stream`, with a HIP event
+ * record before the first kernel (events[0]) and one after every kernel that the call
+ * launches: events[j + 1] follows the j-th kernel launched, whose id (moe_kernel_id) is
+ * written to kernel_ids[j] (host memory); *num_kernels (host) receives the number of kernels
+ * launched (0 for m = 0 and on an argument error). Which kernels run depends on the path: the
+ * decode path packs the routes inside its FC1 launch for small m and has no combine pass.
+ * The caller creates the events (num_events >= 6) and provides room for 5 ids. Not for graph
+ * capture. Errors as moe_w4a16_fused, plus MOE_ERR_INVALID_ARG for too few events or NULL
+ * kernel_ids / num_kernels. */
+typedef enum moe_kernel_id {
+  MOE_KERNEL_ROUTE_PACK = 0,
+  MOE_KERNEL_FC1 = 1,          /* FC1 + activation epilogue */
+  MOE_KERNEL_REQUANT = 2,      /* the W4A8 variant's MXFP8 rounding pass */
+  MOE_KERNEL_FC2 = 3,          /* FC2 (+ the top-k sum on the decode path) */
+  MOE_KERNEL_COMBINE = 4       /* the grouped-GEMM path's top-k combine pass */
+} moe_kernel_id;
+
 int moe_w4a16_fused_profiled(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes,
                              const uint16_t* x, int64_t m, const int32_t* topk_ids,
                              const float* topk_weights, int topk, const int32_t* expert_map,
                              int num_global_experts, int64_t token_capacity, void* workspace,
                              size_t workspace_bytes, uint16_t* out, hipStream_t stream,
-                             hipEvent_t* events, int num_events);
+                             hipEvent_t* events, int num_events, int32_t* kernel_ids,
+                             int* num_kernels);
 
 /* ------------------------------------------------------------------ router front end
  * Page: Summary (New Features: configurable routing) and Walkthrough (kernel compilation and

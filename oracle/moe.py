@@ -45,15 +45,19 @@ class Experts:
     Canonical layout: w13 nibbles [E, N1, H/2], s13 scale bytes [E, N1, ceil(H/G)],
     w2 nibbles [E, H, I/2], s2 [E, H, ceil(I/G)], g13 / g2 fp32 [E] (NVFP4 only).
     ``expert_ids`` maps a row of these arrays to its local expert id when only a
-    subset of experts is held.
+    subset of experts is held. ``cache=False`` decodes on every use and keeps
+    nothing (bounded memory for layers with many large experts; the values are
+    the same either way).
     """
 
-    def __init__(self, fmt: str, act: str, hidden: int, inter: int, codes: dict, expert_ids=None):
+    def __init__(self, fmt: str, act: str, hidden: int, inter: int, codes: dict, expert_ids=None,
+                 cache: bool = True):
         self.fmt, self.act, self.hidden, self.inter = fmt, act, hidden, inter
         self.codes = codes
         n = codes["w13"].shape[0]
         ids = list(range(n)) if expert_ids is None else list(expert_ids)
         self.row = {int(e): i for i, e in enumerate(ids)}
+        self.cache = cache
         self._w13, self._w2 = {}, {}
 
     def _g(self, key, i):
@@ -62,18 +66,22 @@ class Experts:
         return np.asarray(self.codes[key], dtype=np.float32)[i:i + 1]
 
     def w13(self, e: int) -> np.ndarray:
-        if e not in self._w13:
-            i = self.row[e]
-            self._w13[e] = formats.dequant(self.fmt, self.codes["w13"][i:i + 1], self.codes["s13"][i:i + 1],
-                                           self._g("g13", i))[0]
-        return self._w13[e]
+        if e in self._w13:
+            return self._w13[e]
+        i = self.row[e]
+        w = formats.dequant(self.fmt, self.codes["w13"][i:i + 1], self.codes["s13"][i:i + 1], self._g("g13", i))[0]
+        if self.cache:
+            self._w13[e] = w
+        return w
 
     def w2(self, e: int) -> np.ndarray:
-        if e not in self._w2:
-            i = self.row[e]
-            self._w2[e] = formats.dequant(self.fmt, self.codes["w2"][i:i + 1], self.codes["s2"][i:i + 1],
-                                          self._g("g2", i))[0]
-        return self._w2[e]
+        if e in self._w2:
+            return self._w2[e]
+        i = self.row[e]
+        w = formats.dequant(self.fmt, self.codes["w2"][i:i + 1], self.codes["s2"][i:i + 1], self._g("g2", i))[0]
+        if self.cache:
+            self._w2[e] = w
+        return w
 
 
 def fc2_input(a: np.ndarray, mxfp8: bool) -> np.ndarray:

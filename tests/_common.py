@@ -34,6 +34,7 @@ class Case:
     xbits: np.ndarray
     codes: Optional[dict]          # canonical codes on the host (all experts), or None
     codes_dev: Optional[dict] = None
+    key: Optional[tuple] = None    # full-size cases: (workload, m, routing seed, code seed), memoises the oracle
 
 
 def quantised_codes(cfg: C.Workload, rng) -> dict:
@@ -64,15 +65,24 @@ def experts_for(case: Case, experts=None) -> M.Experts:
     cfg = case.cfg
     if case.codes is not None:
         return M.Experts(cfg.fmt, cfg.act, cfg.hidden, cfg.inter, case.codes)
-    # full-size device codes: copy only the experts the oracle needs
+    # full-size device codes: copy only the experts the oracle needs, and keep no dequantised
+    # expert after its use (up to ~150 experts of 350 MB each in float64 at the prefill shape)
     ids = sorted(int(e) for e in experts)
     sub = {k: case.codes_dev[k][ids].cpu().numpy() for k in ("w13", "s13", "w2", "s2", "g13", "g2")}
-    return M.Experts(cfg.fmt, cfg.act, cfg.hidden, cfg.inter, sub, expert_ids=ids)
+    return M.Experts(cfg.fmt, cfg.act, cfg.hidden, cfg.inter, sub, expert_ids=ids, cache=False)
+
+
+# Oracle outputs of full-size cases, by (case key, variant): the same prefill case is checked by
+# more than one test, and its oracle run takes a minute or more.
+_ORACLE_MEMO: dict = {}
 
 
 def oracle_out(case: Case, tokens=None, cols=None, mxfp8: bool = False) -> np.ndarray:
     from oracle.route_pack import local_ids
 
+    memo = case.key is not None and tokens is None and cols is None
+    if memo and (case.key, mxfp8) in _ORACLE_MEMO:
+        return _ORACLE_MEMO[(case.key, mxfp8)]
     cfg = case.cfg
     x = F.bf16_bits_to_f64(case.xbits)
     needed = None
@@ -81,8 +91,23 @@ def oracle_out(case: Case, tokens=None, cols=None, mxfp8: bool = False) -> np.nd
         lid = local_ids(case.ids, case.emap, cfg.num_global_experts, cfg.num_experts).reshape(case.m, cfg.topk)
         needed = np.unique(lid[t][lid[t] >= 0])
     ex = experts_for(case, needed)
-    return M.moe_forward(x, case.ids, case.w, case.emap, cfg.num_global_experts, cfg.num_experts, ex,
-                         tokens=tokens, cols=cols, mxfp8=mxfp8)
+    out = M.moe_forward(x, case.ids, case.w, case.emap, cfg.num_global_experts, cfg.num_experts, ex,
+                        tokens=tokens, cols=cols, mxfp8=mxfp8)
+    if memo:
+        _ORACLE_MEMO[(case.key, mxfp8)] = out
+    return out
+
+
+def full_case(name: str, m: int, device, codes_dev: Optional[dict] = None) -> Case:
+    """A full-size workload case: routing and activations seeded per (workload, m), random
+    canonical codes drawn on the device (seed per workload) unless ``codes_dev`` is given."""
+    cfg = C.get_config(name)
+    seed = cfg.index * 1000 + m
+    case = make_case(cfg, m, seed=seed, weights="none")
+    case.codes_dev = codes_dev if codes_dev is not None else D.draw_random_codes_torch(cfg, seed=1000 + cfg.index,
+                                                                                         device=device)
+    case.key = (name, m, seed, 1000 + cfg.index)
+    return case
 
 
 def bf16_tensor_to_f64(t) -> np.ndarray:

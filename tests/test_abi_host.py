@@ -176,3 +176,47 @@ def test_one_hip_runtime_in_process():
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip() == "1", out.stdout
+
+
+def test_binding_rejects_mismatched_tensors_before_any_call():
+    """int64 ids (what torch.topk returns), transposed views, wrong widths and host tensors are
+    refused by the binding with MOE_ERR_INVALID_ARG instead of being read as wrong data."""
+    torch = pytest.importorskip("torch")
+    d = moe.make_dims("mxfp4", "silu_swiglu", 8, 256, 128)
+    m, k = 4, 2
+    good = dict(x=torch.zeros((m, 256), dtype=torch.bfloat16), topk_ids=torch.zeros((m, k), dtype=torch.int32),
+                topk_weights=torch.zeros((m, k), dtype=torch.float32), out=torch.zeros((m, 256), dtype=torch.bfloat16))
+
+    def code(**kw):
+        a = dict(good)
+        a.update(kw)
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_w4a16_fused(d, 1 << 20, 1 << 30, a["x"], m, a["topk_ids"], a["topk_weights"], k, None, 8, 4,
+                                1 << 20, 1 << 30, a["out"], stream=0)
+        return ei.value.code, str(ei.value)
+
+    c, msg = code(topk_ids=torch.zeros((m, k), dtype=torch.int64))
+    assert c == moe.MOE_ERR_INVALID_ARG and "topk_ids" in msg and "int32" in msg
+    c, msg = code(x=torch.zeros((256, m), dtype=torch.bfloat16).t())
+    assert c == moe.MOE_ERR_INVALID_ARG and "x" in msg
+    c, msg = code(topk_weights=torch.zeros((m, k + 1), dtype=torch.float32))
+    assert c == moe.MOE_ERR_INVALID_ARG and "topk_weights" in msg
+    c, msg = code(out=torch.zeros((m, 256), dtype=torch.float32))
+    assert c == moe.MOE_ERR_INVALID_ARG and "out" in msg
+    c, msg = code()                                              # host tensors of the right kinds
+    assert c == moe.MOE_ERR_INVALID_ARG and "cpu" in msg
+
+
+def test_profiled_twin_validates_its_event_arguments():
+    d = moe.make_dims("mxfp4", "silu_swiglu", 8, 256, 128)
+    lib = moe.lib()
+    ids = (ctypes.c_int32 * 5)()
+    n = ctypes.c_int(7)
+    ev = (ctypes.c_void_p * 5)()
+    rc = lib.moe_w4a16_fused_profiled(ctypes.byref(d), 1 << 20, 1 << 30, 1 << 20, 4, 1 << 20, 1 << 20, 2, None, 8, 4,
+                                      1 << 20, 1 << 30, 1 << 20, None, ev, 5, ids, ctypes.byref(n))
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    ev6 = (ctypes.c_void_p * 6)()
+    rc = lib.moe_w4a16_fused_profiled(ctypes.byref(d), 1 << 20, 1 << 30, 1 << 20, 4, 1 << 20, 1 << 20, 2, None, 8, 4,
+                                      1 << 20, 1 << 30, 1 << 20, None, ev6, 6, None, ctypes.byref(n))
+    assert rc == moe.MOE_ERR_INVALID_ARG
