@@ -26,6 +26,7 @@ MOE_FMT_MXFP4_E8M0_K32 = 2
 MOE_ACT_SILU_SWIGLU = 1
 MOE_ACT_RELU2 = 2
 MOE_DECODE_MAX_M = 16
+MOE_STATIC_WORKSPACE_BYTES = 64 << 20
 
 FMT = {"nvfp4": MOE_FMT_NVFP4_E4M3_K16, "mxfp4": MOE_FMT_MXFP4_E8M0_K32}
 ACT = {"silu_swiglu": MOE_ACT_SILU_SWIGLU, "relu2": MOE_ACT_RELU2}
@@ -82,6 +83,7 @@ def _load():
         "moe_w4a16_fused": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
         "moe_w4a8_fused": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
         "moe_w4a16_fused_atomic_bf16": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
+        "moe_w4a16_fused_static_workspace": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, P]),
         "moe_w4a16_fused_profiled": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P, P, I32,
                                            ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int)]),
         "moe_last_error": (ctypes.c_char_p, []),
@@ -100,7 +102,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("moe_route_pack_token_capacity", "moe_route_pack_workspace_size", "moe_route_pack",
             "moe_w4a16_prepared_size", "moe_w4a16_prepare", "moe_w4a16_workspace_size", "moe_w4a16_fused",
-            "moe_w4a8_fused", "moe_w4a16_fused_atomic_bf16",
+            "moe_w4a8_fused", "moe_w4a16_fused_atomic_bf16", "moe_w4a16_fused_static_workspace",
             "moe_w4a16_fused_profiled", "moe_last_error", "moe_w4a16_set_path", "moe_w4a16_set_decode_max_m",
             "moe_router_topk", "moe_w4a16_prepare_layout")
 
@@ -248,6 +250,18 @@ def moe_w4a16_fused_atomic_bf16(dims: moe_w4a16_dims, prepared, prepared_bytes: 
                                             _ptr(topk_ids), _ptr(topk_weights), topk, _ptr(expert_map),
                                             num_global_experts, token_capacity, _ptr(workspace), workspace_bytes,
                                             _ptr(out), _stream(stream)), "moe_w4a16_fused_atomic_bf16")
+
+
+def moe_w4a16_fused_static_workspace(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: int, topk_ids,
+                                     topk_weights, topk: int, expert_map, num_global_experts: int,
+                                     token_capacity: int, out, stream=None) -> None:
+    """moe_w4a16_fused with the library's own device workspace (no caller workspace, no allocation)."""
+    _check_fused_args(dims, x, m, topk_ids, topk_weights, topk, expert_map, num_global_experts, out,
+                      "moe_w4a16_fused_static_workspace")
+    _check(_lib.moe_w4a16_fused_static_workspace(ctypes.byref(dims), _ptr(prepared), prepared_bytes, _ptr(x), m,
+                                                 _ptr(topk_ids), _ptr(topk_weights), topk, _ptr(expert_map),
+                                                 num_global_experts, token_capacity, _ptr(out), _stream(stream)),
+           "moe_w4a16_fused_static_workspace")
 
 
 KERNEL_NAMES = ("route_pack", "fc1", "requant", "fc2", "combine")    # moe_kernel_id order

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_w4a16.so")
-SOURCES = ["api.cpp", "route_pack.hip", "prepare.hip", "decode.hip", "gemm.hip", "router.hip", "requant.hip"]
+SOURCES = ["api.cpp", "route_pack.hip", "prepare.hip", "decode.hip", "gemm.hip", "router.hip", "requant.hip", "static_workspace.hip"]
 HEADERS = ["layout.hpp", "device.hpp", "kernels.hpp"]
 
 

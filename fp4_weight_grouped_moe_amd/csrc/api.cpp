@@ -20,14 +20,19 @@ namespace {
 
 thread_local std::string g_last_error;
 
-int fail(int code, const char* fmt, ...) {
+int vfail(int code, const char* fmt, va_list ap) {
   char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
   g_last_error = buf;
   return code;
+}
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int rc = vfail(code, fmt, ap);
+  va_end(ap);
+  return rc;
 }
 
 int ok() {
@@ -126,6 +131,14 @@ int launch_status(hipError_t e, const char* what) {
 }
 
 }  // namespace
+
+int moe::report_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int rc = vfail(code, fmt, ap);
+  va_end(ap);
+  return rc;
+}
 
 extern "C" {
 

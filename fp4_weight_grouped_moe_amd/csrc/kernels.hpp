@@ -90,6 +90,9 @@ struct FusedParams {
   int64_t xs_pitch;              // decode FC1: elements per staged activation row in LDS
 };
 
+// Sets the message moe_last_error() returns on this thread; returns `code`.
+int report_error(int code, const char* fmt, ...);
+
 // Router front end: top-k of fp32 logits [m, num_experts] per token.
 struct RouterParams {
   const float* logits;

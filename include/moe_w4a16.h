@@ -225,6 +225,25 @@ int moe_w4a16_fused_atomic_bf16(const moe_w4a16_dims* dims, const void* prepared
                                 int64_t token_capacity, void* workspace, size_t workspace_bytes,
                                 uint16_t* out, hipStream_t stream);
 
+/* Allocation-free variant, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. moe_w4a16_fused with
+ * its workspace in a device array the library itself holds: MOE_STATIC_WORKSPACE_BYTES on each
+ * GPU the library runs on, from the load of its code object until the process ends. Arguments,
+ * layouts, ownership and results as moe_w4a16_fused, without the workspace arguments; the call
+ * allocates and frees nothing. Errors as moe_w4a16_fused, and MOE_ERR_WORKSPACE, before any
+ * device work, when the layer at token_capacity needs more workspace than the array holds
+ * (moe_w4a16_workspace_size gives the need; 64 MiB covers, e.g., the 128-expert
+ * hidden-4096 decode shape up to a capacity of 64 tokens). All calls on one GPU share its
+ * array, which keeps the last call's contents: calls that overlap on one GPU (other streams
+ * or threads) race and must be serialised by the caller. */
+#define MOE_STATIC_WORKSPACE_BYTES (64u << 20)
+
+int moe_w4a16_fused_static_workspace(const moe_w4a16_dims* dims, const void* prepared,
+                                     size_t prepared_bytes, const uint16_t* x, int64_t m,
+                                     const int32_t* topk_ids, const float* topk_weights, int topk,
+                                     const int32_t* expert_map, int num_global_experts,
+                                     int64_t token_capacity, uint16_t* out, hipStream_t stream);
+
 /* ------------------------------------------------------------------ diagnostics */
 
 /* Measurement twin of moe_w4a16_fused: the same launches on `stream`, with a HIP event
