@@ -7,7 +7,7 @@ rotate through distinct routing batches, so consecutive steps touch different ex
 way consecutive decode steps do.
 
 Timings of each workload and token count m:
-  cold      each call bracketed by its own HIP event pair, with a 512 MiB scratch write
+  cold      each call bracketed by its own HIP event pair, with a 512 MiB scratch read
             before it (outside the timed region) so that neither the L2s nor the 256 MiB
             Infinity Cache hold the previous call's weights; the median over the steps.
   warm      the same calls back to back, one event pair around all of them (mean).
@@ -41,6 +41,12 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 / f16 MFMA
 SCRATCH_BYTES = 512 << 20       # cold protocol: written between calls
 PASSES = ("cold", "warm", "graph", "profiled")
+_T0 = time.time()
+
+
+def log(msg):
+    """A progress line on stderr (the JSON result is the one line on stdout)."""
+    print(f"[bench {time.time() - _T0:6.1f} s] {msg}", file=sys.stderr, flush=True)
 
 
 def parse():
@@ -55,6 +61,8 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="headline only (no decode m = 1 / 4 and prefill entries)")
     ap.add_argument("--sweep-steps", type=int, default=50, help="timed steps of each sweep entry (each pass)")
     ap.add_argument("--sweep-warmup", type=int, default=10)
+    ap.add_argument("--flush", default="read", choices=["read", "write"],
+                    help="cold protocol: read (default) or write 512 MiB of scratch between calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--w4a8", action="store_true",
                     help="time the W4A8 variant (moe_w4a8_fused, MXFP4 workloads): whole-layer time only")
@@ -155,6 +163,7 @@ class Layer:
         moe.moe_w4a16_prepare(self.dims, c["w13"], c["s13"], c["g13"] if nv else None, c["w2"], c["s2"],
                               c["g2"] if nv else None, self.prepared, self.prepared_bytes)
         torch.cuda.synchronize()
+        log(f"{cfg.name}: weights drawn and prepared")
 
 
 def measure(layer, m, steps, warmup, args, passes):
@@ -191,7 +200,9 @@ def measure(layer, m, steps, warmup, args, passes):
     out = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
     ws_bytes = moe.moe_w4a16_workspace_size(layer.dims, cap, k)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    scratch = torch.empty(SCRATCH_BYTES, dtype=torch.uint8, device=dev)
+    scratch = torch.zeros(SCRATCH_BYTES, dtype=torch.uint8, device=dev)
+    scratch_words = scratch.view(torch.int32)
+    flush_sink = torch.zeros((), dtype=torch.int64, device=dev)
 
     # raw pointers resolved once, so that the host launch rate does not limit small steps
     lib = moe.lib()
@@ -212,9 +223,16 @@ def measure(layer, m, steps, warmup, args, passes):
             raise moe.MoeError(rc, "fused call", moe.moe_last_error())
 
     def cold_fill(i):
-        scratch.fill_(i & 0xFF)
+        # Evict the previous calls' weights from the L2s and the 256 MiB Infinity Cache by
+        # reading 512 MiB (reads allocate there). A write would leave up to 256 MiB of dirty
+        # lines whose write-back then falls inside the next timed call.
+        if args.flush == "write":
+            scratch.fill_(i & 0xFF)
+        else:
+            torch.sum(scratch_words, dim=0, dtype=torch.int64, out=flush_sink)
 
     res = {"m": m, "token_capacity": cap, "routing_sets": sets}
+    log(f"{cfg.name} m={m}: {sets} routing batches ready")
     stream = torch.cuda.current_stream().cuda_stream
     moe.moe_w4a16_set_path(args.path)
     try:
@@ -233,6 +251,7 @@ def measure(layer, m, steps, warmup, args, passes):
                 ev[i][1].record()
             torch.cuda.synchronize()
             t = np.array([a.elapsed_time(b) for a, b in ev])
+            log(f"{cfg.name} m={m}: cold pass done, median {np.median(t):.4f} ms")
             res["cold"] = {"ms_median": round(float(np.median(t)), 5), "ms_p10": round(float(np.percentile(t, 10)), 5),
                            "ms_p90": round(float(np.percentile(t, 90)), 5), "samples": steps}
 
@@ -244,6 +263,7 @@ def measure(layer, m, steps, warmup, args, passes):
                 call(warmup + i, stream)
             e1.record()
             torch.cuda.synchronize()
+            log(f"{cfg.name} m={m}: warm pass done")
             res["warm"] = {"ms_mean": round(e0.elapsed_time(e1) / steps, 5), "samples": steps,
                            "note": "back to back, rotating routing batches"}
 
@@ -264,6 +284,7 @@ def measure(layer, m, steps, warmup, args, passes):
                 graphs[i % n_graphs].replay()
             e1.record()
             torch.cuda.synchronize()
+            log(f"{cfg.name} m={m}: graph pass done")
             res["graph"] = {"ms_mean": round(e0.elapsed_time(e1) / steps, 5), "samples": steps,
                             "note": f"HIP graph replay back to back, {n_graphs} routing batches"}
             del graphs
@@ -288,6 +309,7 @@ def measure(layer, m, steps, warmup, args, passes):
                 for j, name in enumerate(names[i]):
                     per.setdefault(name, []).append(hev.elapsed_ms(hev.ev[6 * i + j], hev.ev[6 * i + j + 1]))
             res["kernel_us"] = {n: round(float(np.mean(v)) * 1e3, 2) for n, v in per.items()}
+            log(f"{cfg.name} m={m}: profiled pass done {res['kernel_us']}")
             res["kernels_launched"] = names[0]
             del hev
     finally:
@@ -344,7 +366,7 @@ def measure(layer, m, steps, warmup, args, passes):
             "avg_launch_us": round(float(np.mean(per[dom])) * 1e3, 2)}
     res["workload"] = (f"{cfg.name}: E{cfg.num_experts} H{H} I{cfg.inter} top{k} {cfg.fmt.upper()} {cfg.act} m={m}")
     res["_batches"] = (ids_l, w_l, x_l, emap)
-    del d_ids, d_w, d_x, out, ws, scratch
+    del d_ids, d_w, d_x, out, ws, scratch, scratch_words, flush_sink
     torch.cuda.empty_cache()
     return res
 
@@ -453,15 +475,19 @@ def cpu_baseline(layer, m, batches, target_s):
         ex = M.Experts(cfg.fmt, cfg.act, cfg.hidden, cfg.inter, host, expert_ids=need, cache=False)
         t0 = time.perf_counter()
         M.moe_forward(x, ids, w, emap, cfg.num_global_experts, cfg.num_experts, ex, tokens=toks)
-        return time.perf_counter() - t0
+        dt = time.perf_counter() - t0
+        log(f"{cfg.name}: oracle on {n} tokens of batch {b} took {dt:.1f} s")
+        return dt
 
-    # a prefix of the first batch, grown until it takes the target time or covers the batch
+    # a prefix of the first batch, grown (at least doubling: the oracle's time grows more slowly
+    # than its token count, as more tokens share the dequantised experts) until it takes about
+    # the target time or covers the batch
     n, elapsed = 1, 0.0
     while True:
         elapsed = run(0, n)
-        if elapsed >= target_s or n >= m:
+        if elapsed >= 0.6 * target_s or n >= m:
             break
-        n = min(m, max(n + 1, int(np.ceil(n * target_s / max(elapsed, 1e-3)))))
+        n = min(m, max(2 * n, int(np.ceil(n * target_s / max(elapsed, 1e-3)))))
     tokens, nb = n, 1
     # whole batches are short: add the next routing batches up to the target
     while n == m and elapsed < target_s and nb < len(ids_l):

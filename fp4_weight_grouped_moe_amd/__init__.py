@@ -82,6 +82,7 @@ def _load():
         "moe_w4a16_workspace_size": (I32, [PD, I64, I32, PSZ]),
         "moe_w4a16_fused": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
         "moe_w4a8_fused": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
+        "moe_w4a16_fused_device_m": (I32, [PD, P, SZ, P, P, P, P, I32, P, I32, I64, P, SZ, P, P]),
         "moe_w4a16_fused_atomic_bf16": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P]),
         "moe_w4a16_fused_static_workspace": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, P]),
         "moe_w4a16_fused_profiled": (I32, [PD, P, SZ, P, I64, P, P, I32, P, I32, I64, P, SZ, P, P, P, I32,
@@ -89,6 +90,7 @@ def _load():
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_w4a16_set_path": (I32, [I32]),
         "moe_w4a16_set_decode_max_m": (I32, [I32]),
+        "moe_w4a16_set_grid_limit": (I32, [I32]),
         "moe_router_topk": (I32, [P, I64, I32, I32, I32, I32, P, P, P]),
         "moe_w4a16_prepare_layout": (I32, [PD, ctypes.POINTER(moe_w4a16_source_layout), P, P, P, P, P, P, P, SZ, P]),
     }
@@ -103,7 +105,9 @@ _lib = _load()
 EXPORTED = ("moe_route_pack_token_capacity", "moe_route_pack_workspace_size", "moe_route_pack",
             "moe_w4a16_prepared_size", "moe_w4a16_prepare", "moe_w4a16_workspace_size", "moe_w4a16_fused",
             "moe_w4a8_fused", "moe_w4a16_fused_atomic_bf16", "moe_w4a16_fused_static_workspace",
+            "moe_w4a16_fused_device_m",
             "moe_w4a16_fused_profiled", "moe_last_error", "moe_w4a16_set_path", "moe_w4a16_set_decode_max_m",
+            "moe_w4a16_set_grid_limit",
             "moe_router_topk", "moe_w4a16_prepare_layout")
 
 
@@ -233,6 +237,21 @@ def moe_w4a16_fused(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: i
                                 _ptr(workspace), workspace_bytes, _ptr(out), _stream(stream)), "moe_w4a16_fused")
 
 
+def moe_w4a16_fused_device_m(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m_device, topk_ids,
+                             topk_weights, topk: int, expert_map, num_global_experts: int, token_capacity: int,
+                             workspace, workspace_bytes: int, out, stream=None) -> None:
+    """The fused layer with m read from the device int32 ``m_device`` when the call runs; x,
+    topk_ids, topk_weights and out hold token_capacity rows (rows at or past m of out become 0)."""
+    import torch
+    _check_fused_args(dims, x, token_capacity, topk_ids, topk_weights, topk, expert_map, num_global_experts, out,
+                      "moe_w4a16_fused_device_m")
+    _require(m_device, "m_device", torch.int32, 1, None, None, "moe_w4a16_fused_device_m")
+    _check(_lib.moe_w4a16_fused_device_m(ctypes.byref(dims), _ptr(prepared), prepared_bytes, _ptr(x), _ptr(m_device),
+                                         _ptr(topk_ids), _ptr(topk_weights), topk, _ptr(expert_map),
+                                         num_global_experts, token_capacity, _ptr(workspace), workspace_bytes,
+                                         _ptr(out), _stream(stream)), "moe_w4a16_fused_device_m")
+
+
 def moe_w4a8_fused(dims: moe_w4a16_dims, prepared, prepared_bytes: int, x, m: int, topk_ids, topk_weights,
                    topk: int, expert_map, num_global_experts: int, token_capacity: int, workspace,
                    workspace_bytes: int, out, stream=None) -> None:
@@ -309,6 +328,10 @@ def moe_w4a16_set_path(path) -> int:
 
 def moe_w4a16_set_decode_max_m(max_m: int) -> int:
     return _check(_lib.moe_w4a16_set_decode_max_m(int(max_m)), "moe_w4a16_set_decode_max_m")
+
+
+def moe_w4a16_set_grid_limit(max_cus: int) -> int:
+    return _check(_lib.moe_w4a16_set_grid_limit(int(max_cus)), "moe_w4a16_set_grid_limit")
 
 
 class MoeLayer:

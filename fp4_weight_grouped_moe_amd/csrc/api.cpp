@@ -61,6 +61,7 @@ int initial_decode_max_m() {
 std::mutex g_cfg_mu;
 int g_path = initial_path();
 int g_decode_max_m = initial_decode_max_m();
+int g_grid_limit = 0;           // 0: launch for every CU of the device
 
 struct DeviceInfo {
   bool probed = false;
@@ -176,6 +177,7 @@ int moe_route_pack(const int32_t* topk_ids, int64_t m, int topk, const int32_t* 
   rp.topk_ids = topk_ids;
   rp.topk_weights = nullptr;
   rp.expert_map = expert_map;
+  rp.m_dev = nullptr;
   rp.m = m;
   rp.num_routes = m * topk;
   rp.cap_k = token_capacity * topk;
@@ -264,7 +266,8 @@ namespace {
 int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes, const uint16_t* x, int64_t m,
                const int32_t* topk_ids, const float* topk_weights, int topk, const int32_t* expert_map,
                int num_global_experts, int64_t token_capacity, void* workspace, size_t workspace_bytes, uint16_t* out,
-               hipStream_t stream, LaunchMarks* marks, bool w4a8 = false, bool atomic_bf16 = false) {
+               hipStream_t stream, LaunchMarks* marks, bool w4a8 = false, bool atomic_bf16 = false,
+               const int32_t* m_dev = nullptr) {
   if (int rc = check_dims(dims)) return rc;
   if (w4a8 && dims->fmt != MOE_FMT_MXFP4_E8M0_K32)
     return fail(MOE_ERR_UNSUPPORTED, "the W4A8 variant needs MXFP4 weights (E8M0 block scales)");
@@ -282,11 +285,12 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
     if (!x || !topk_ids || !topk_weights || !out) return fail(MOE_ERR_INVALID_ARG, "x, topk_ids, topk_weights and out must be non-NULL");
     if (!aligned(x, 16) || !aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "x and out must be 16-byte aligned");
   }
-  int path, dmax;
+  int path, dmax, grid_limit;
   {
     std::lock_guard<std::mutex> lk(g_cfg_mu);
     path = g_path;
     dmax = g_decode_max_m;
+    grid_limit = g_grid_limit;
   }
   const bool decode = path == 1 || (path == 0 && m <= dmax && token_capacity <= kDecodeMaxM);
   if (decode && token_capacity > kDecodeMaxM)
@@ -299,6 +303,7 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   int cus = 0;
   if (int rc = check_device(&cus)) return rc;
   if (m == 0) return ok();
+  if (grid_limit > 0 && grid_limit < cus) cus = grid_limit;   // launches sized as for that many CUs
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* pk = ws + fg.off_pack;
@@ -307,6 +312,7 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   rp.topk_ids = topk_ids;
   rp.topk_weights = topk_weights;
   rp.expert_map = expert_map;
+  rp.m_dev = m_dev;
   rp.m = m;
   rp.num_routes = m * topk;
   rp.cap_k = token_capacity * topk;
@@ -347,6 +353,7 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   fp.x = x;
   fp.out = out;
   fp.m = m;
+  fp.m_dev = m_dev;
   fp.topk = topk;
   fp.sorted_route_ids = rp.sorted_route_ids;
   fp.block_expert = rp.block_expert;
@@ -395,6 +402,19 @@ int moe_w4a16_fused(const moe_w4a16_dims* dims, const void* prepared, size_t pre
                     size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
   return fused_impl(dims, prepared, prepared_bytes, x, m, topk_ids, topk_weights, topk, expert_map,
                     num_global_experts, token_capacity, workspace, workspace_bytes, out, stream, nullptr);
+}
+
+int moe_w4a16_fused_device_m(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes,
+                             const uint16_t* x, const int32_t* m_device, const int32_t* topk_ids,
+                             const float* topk_weights, int topk, const int32_t* expert_map, int num_global_experts,
+                             int64_t token_capacity, void* workspace, size_t workspace_bytes, uint16_t* out,
+                             hipStream_t stream) {
+  if (!m_device || !aligned(m_device, 4)) return fail(MOE_ERR_INVALID_ARG, "m_device must be a 4-byte aligned device pointer");
+  if (int rc = check_capacity(token_capacity)) return rc;
+  // Every launch is sized for token_capacity tokens; the kernels read the live count.
+  return fused_impl(dims, prepared, prepared_bytes, x, token_capacity, topk_ids, topk_weights, topk, expert_map,
+                    num_global_experts, token_capacity, workspace, workspace_bytes, out, stream, nullptr, false, false,
+                    m_device);
 }
 
 int moe_w4a8_fused(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes, const uint16_t* x,
@@ -461,6 +481,14 @@ int moe_router_topk(const float* logits, int64_t m, int num_experts, int topk, i
   p.topk_ids = topk_ids;
   p.topk_weights = topk_weights;
   return launch_status(launch_router(p, stream), "router launch");
+}
+
+int moe_w4a16_set_grid_limit(int max_cus) {
+  if (max_cus < 0) return fail(MOE_ERR_INVALID_ARG, "grid limit %d is negative", max_cus);
+  std::lock_guard<std::mutex> lk(g_cfg_mu);
+  int prev = g_grid_limit;
+  g_grid_limit = max_cus;
+  return prev;
 }
 
 int moe_w4a16_set_decode_max_m(int max_m) {

@@ -147,12 +147,13 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
     for (int e = tid; e < g.E; e += kF1Threads) cnt[e] = 0;
     for (int s = tid; s < nbmax * kBlockM; s += kF1Threads) sroute[s] = -1;
     if (wave == 0) {
+      const int rl = int(routes_in_use(p, p.m, p.topk));   // routes past rl are dropped
       int gid[kF1PackRoutes / 64];
       float wt[kF1PackRoutes / 64];
 #pragma unroll
       for (int i = 0; i < kF1PackRoutes / 64; ++i) {
         const int r = lane + 64 * i;
-        gid[i] = r < R ? p.topk_ids[r] : -1;
+        gid[i] = r < rl ? p.topk_ids[r] : -1;
         wt[i] = r < R ? p.topk_weights[r] : 0.f;
       }
 #pragma unroll
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
         p.live[0] = nvalid;
         p.live[1] = total;
         p.live[2] = live_blocks;
-        p.live[3] = int(p.m);
+        p.live[3] = int(routes_in_use(p, p.m, p.topk) / p.topk);
       }
     }
     if (live_blocks * n_it <= int(blockIdx.x)) return;        // no item for this workgroup

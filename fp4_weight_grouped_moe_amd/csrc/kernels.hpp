@@ -12,6 +12,9 @@ struct RoutePackParams {
   const int32_t* topk_ids;       // [m * topk]
   const float* topk_weights;     // [m * topk] or null (only the fused layer passes it)
   const int32_t* expert_map;     // [num_global_experts] or null
+  // Token count read on the device (or null): routes of tokens at or past *m_dev are dropped,
+  // and m / num_routes above are then the capacity's bounds.
+  const int32_t* m_dev;
   int64_t m, num_routes, cap_k, cap_routes, cap_blocks;
   int32_t topk, num_global_experts, num_experts, block_m;
   int32_t* expert_counts;
@@ -57,6 +60,7 @@ struct FusedParams {
   const uint16_t* x;             // bf16 [m, H]
   uint16_t* out;                 // bf16 [m, H]
   int64_t m;
+  const int32_t* m_dev;          // token count read on the device (or null; m is then its bound)
   int32_t topk;
   int32_t* sorted_route_ids;
   int32_t* block_expert;
@@ -89,6 +93,15 @@ struct FusedParams {
   int64_t cap_blocks;
   int64_t xs_pitch;              // decode FC1: elements per staged activation row in LDS
 };
+
+// Routes in use: m * topk, or with a device token count min(max(*m_dev, 0), m) * topk (the
+// value was written before the launch, so every lane reads the same).
+template <typename P>
+__device__ __forceinline__ int64_t routes_in_use(const P& p, int64_t m, int topk) {
+  if (!p.m_dev) return m * topk;
+  const int64_t v = *p.m_dev;
+  return (v < 0 ? 0 : (v > m ? m : v)) * topk;
+}
 
 // Sets the message moe_last_error() returns on this thread; returns `code`.
 int report_error(int code, const char* fmt, ...);

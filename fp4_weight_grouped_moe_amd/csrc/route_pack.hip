@@ -26,8 +26,9 @@ __host__ __device__ inline size_t route_pack_base_lds(int num_experts) {
 }
 constexpr int kRowRegs = 8;                    // 16-byte chunks per lane per batch of the row conversion
 
-__device__ __forceinline__ int local_expert(const RoutePackParams& p, int64_t r) {
-  if (r >= p.num_routes) return -1;
+// Local expert of route r, or -1 (r at or past the routes in use `rl`, an invalid or unmapped id).
+__device__ __forceinline__ int local_expert(const RoutePackParams& p, int64_t r, int64_t rl) {
+  if (r >= rl) return -1;
   int g = p.topk_ids[r];
   if (g < 0 || g >= p.num_global_experts) return -1;
   int l = p.expert_map ? p.expert_map[g] : g;
@@ -74,7 +75,7 @@ __host__ __device__ inline bool slot_map_pass(int64_t num_routes, int num_expert
          block_map_offset(num_experts, cap_routes) + size_t(cap_routes / block_m) * 2 <= kPackLdsMax;
 }
 
-__device__ void cache_routes(const RoutePackParams& p, int16_t* lc, int* cnt) {
+__device__ void cache_routes(const RoutePackParams& p, int16_t* lc, int* cnt, int64_t rl) {
   const int tid = threadIdx.x;
   const int64_t R = p.num_routes;
   for (int64_t base = 0; base < R; base += int64_t(kPackThreads) * kLoadBatch) {
@@ -82,7 +83,7 @@ __device__ void cache_routes(const RoutePackParams& p, int16_t* lc, int* cnt) {
 #pragma unroll
     for (int j = 0; j < kLoadBatch; ++j) {
       const int64_t r = base + j * kPackThreads + tid;
-      g[j] = r < R ? p.topk_ids[r] : -1;
+      g[j] = r < rl ? p.topk_ids[r] : -1;
     }
 #pragma unroll
     for (int j = 0; j < kLoadBatch; ++j) {
@@ -169,6 +170,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   int* wave_tot = cnt + E;                                 // [40] scan scratch; [kValidSlot] = valid routes
   int* ecnt = wave_tot + 40;                               // [E] counts (kept for the tile table)
   uint8_t* wcnt = reinterpret_cast<uint8_t*>(ecnt + E);    // [kPackWaves][E] per-wave counts
+  const int64_t rl = routes_in_use(p, p.m, p.topk);         // routes past rl are dropped
   const bool cached = segmented_pack(p.num_routes, E);
   const bool slot_pass = slot_map_pass(p.num_routes, E, p.cap_routes, B);
   int16_t* lc = reinterpret_cast<int16_t*>(smem + route_pack_base_lds(E));                          // [R] local ids
@@ -180,7 +182,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   // Small batches (one chunk) keep the first chunk's local id and router weight in
   // registers; larger ones up to kCacheRoutes keep every route's in LDS. Either way
   // topk_ids / expert_map / topk_weights are read from memory once.
-  const int l_first = cached ? -1 : local_expert(p, tid);
+  const int l_first = cached ? -1 : local_expert(p, tid, rl);
   const float w_first = (!cached && p.topk_weights && tid < p.num_routes) ? p.topk_weights[tid] : 0.f;
   for (int e = tid; e < E; e += kPackThreads) cnt[e] = 0;
   if (tid == 0) wave_tot[kValidSlot] = 0;
@@ -191,11 +193,11 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
     for (int i = tid; i < kPackWaves * E; i += kPackThreads) wmask[i] = 0;
   __syncthreads();
   if (cached) {
-    cache_routes(p, lc, cnt);
+    cache_routes(p, lc, cnt, rl);
   } else {
     if (l_first >= 0) atomicAdd(&cnt[l_first], 1);
     for (int64_t r = kPackThreads + tid; r < p.num_routes; r += kPackThreads) {
-      int l = local_expert(p, r);
+      int l = local_expert(p, r, rl);
       if (l >= 0) atomicAdd(&cnt[l], 1);
     }
   }
@@ -255,7 +257,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
     p.expert_offsets[E] = total_padded;
     p.live[1] = total_padded;
     p.live[2] = total_padded / B;
-    p.live[3] = int(p.m);
+    p.live[3] = int(rl / p.topk);
     p.live[4] = tile_carry;
     p.live[5] = full_tiles;
   }
@@ -394,7 +396,7 @@ __device__ void pack_routes(const RoutePackParams& p, uint8_t* smem) {
   // ids, then add the counts of lower waves of the chunk and the running slot.
   for (int64_t base = 0; base < (cached ? 0 : p.num_routes); base += kPackThreads) {
     const int64_t r = base + tid;
-    const int l = base == 0 ? l_first : local_expert(p, r);
+    const int l = base == 0 ? l_first : local_expert(p, r, rl);
     // Stable rank among the wave's earlier lanes with the same expert, and the wave's count
     // per expert (written by the expert's first lane): one pass over the 64 lanes' ids.
     int rank = 0, same = 0;

@@ -190,6 +190,26 @@ int moe_w4a16_fused(const moe_w4a16_dims* dims, const void* prepared, size_t pre
                     int num_global_experts, int64_t token_capacity, void* workspace,
                     size_t workspace_bytes, uint16_t* out, hipStream_t stream);
 
+/* The same layer with the token count read from device memory when the call executes, so that
+ * one captured HIP graph serves every m up to the capacity (page: Description, shape-stable
+ * route packing on a power-of-two capacity, so that batch-size changes need no new launch
+ * shapes; b12x PR 136: capture-safe small-M dispatch). m = min(max(*m_device, 0),
+ * token_capacity), where m_device is a device int32 written before the call runs (e.g. by a
+ * copy between graph replays). Every launch is sized for token_capacity tokens: x, topk_ids,
+ * topk_weights and out must hold token_capacity rows; rows at or past m of the inputs are
+ * never used for the result (x rows may be read), routes of those tokens are dropped, and rows
+ * m .. token_capacity - 1 of out are written with zeros. The path follows token_capacity (the
+ * decode path when it is at most the decode threshold and MOE_DECODE_MAX_M). On the grouped-GEMM
+ * path the result equals moe_w4a16_fused at that m bit for bit; on the decode path it is the
+ * same layer, equal within the layer's tolerance (the kernels' launch shapes follow the
+ * capacity, which can change the order of the top-k sums). Other arguments, ownership and
+ * errors as moe_w4a16_fused, plus MOE_ERR_INVALID_ARG for a NULL or misaligned m_device. */
+int moe_w4a16_fused_device_m(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes,
+                             const uint16_t* x, const int32_t* m_device, const int32_t* topk_ids,
+                             const float* topk_weights, int topk, const int32_t* expert_map,
+                             int num_global_experts, int64_t token_capacity, void* workspace,
+                             size_t workspace_bytes, uint16_t* out, hipStream_t stream);
+
 /* W4A8 variant of the same layer. Page: PR 4255 review (a grouped MXFP8 quantisation of the
  * SiLU-mul output, checked against a Torch reference with the exact silu). The activation
  * output of every route is rounded to MXFP8 before FC2 -- E4M3FN elements, one E8M0 scale per
@@ -309,6 +329,15 @@ int moe_w4a16_set_path(int path);
  * every m up to it; MOE_W4A16_DECODE_MAX_M overrides it at load).
  * Values outside [0, MOE_DECODE_MAX_M] are rejected. Returns the previous value. */
 int moe_w4a16_set_decode_max_m(int max_m);
+
+/* Test setting: later fused calls size their persistent and grid-stride launches (the grouped
+ * GEMM's FC1 and FC2, the decode path's FC1, the route pack's conversion workgroups) as if the
+ * device had at most max_cus compute units; 0 (the default) uses every CU. With a limit of one,
+ * a single workgroup works through every item of the grouped GEMM. Results are identical bit
+ * for bit at every limit: no workgroup waits for another, so none relies on co-residency (the
+ * page's m = 2048 stall came from grid-wide barriers without a cooperative launch; PR 4255,
+ * Performance). Negative values are rejected. Returns the previous value. */
+int moe_w4a16_set_grid_limit(int max_cus);
 
 #ifdef __cplusplus
 }

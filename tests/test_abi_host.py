@@ -164,6 +164,10 @@ def test_path_and_threshold_setters():
     assert moe.moe_w4a16_set_decode_max_m(old) == 4
     with pytest.raises(moe.MoeError):
         moe.moe_w4a16_set_decode_max_m(17)
+    old = moe.moe_w4a16_set_grid_limit(3)
+    assert moe.moe_w4a16_set_grid_limit(old) == 3
+    with pytest.raises(moe.MoeError):
+        moe.moe_w4a16_set_grid_limit(-1)
 
 
 def test_one_hip_runtime_in_process():

@@ -185,3 +185,98 @@ def test_graph_replay_atomic_bf16_combine(moe, device, name, m):
         moe.moe_w4a16_set_path("auto")
     del layer
     torch.cuda.empty_cache()
+
+
+def _full_or_scaled(name):
+    from synth import configs as C
+    return SCALED[name] if name in SCALED else C.get_config(name)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,cap,ms", [("edge_s", 512, (300, 511, 512, 1, 0)), ("prefill_s", 512, (257, 512, 40)),
+                                         ("decode_s", 16, (1, 9, 16, 4)), ("small_s", 16, (16, 3)),
+                                         ("edge", 512, (300, 511, 512))])
+def test_graph_replay_across_m_on_one_capacity(moe, device, name, cap, ms):
+    """moe_w4a16_fused_device_m captured once at a power-of-two capacity and replayed for several
+    token counts m <= capacity written into a device int32 between replays (the page's reason for
+    the power-of-two route capacity: batch-size changes need no new launch shapes). Input rows at
+    or past m hold junk routed to a valid expert, which must not reach the result; output rows
+    past m must be zero. Each replay equals the eager moe_w4a16_fused call at that m -- bit for bit
+    on the grouped-GEMM path -- and matches the oracle on every output. `edge` is the full-size
+    edge workload (expert map, -1 ids, I = 1400) at capacity 512, rerun at m = 300, 511 and 512."""
+    import torch
+
+    from _common import full_case
+
+    cfg = _full_or_scaled(name)
+    full = name not in SCALED
+    print(f"graph across m {name} capacity {cap} m={ms}", flush=True)
+    base = full_case(name, ms[0], device) if full else make_case(cfg, ms[0], seed=cfg.index * 29 + 1, weights="normal")
+    layer = make_layer(base, device, token_capacity=cap)
+    H, k = cfg.hidden, cfg.topk
+    x = torch.empty((cap, H), dtype=torch.bfloat16, device=device)
+    ids = torch.empty((cap, k), dtype=torch.int32, device=device)
+    wts = torch.empty((cap, k), dtype=torch.float32, device=device)
+    emap = torch.empty(cfg.num_global_experts, dtype=torch.int32, device=device) if base.emap is not None else None
+    m_dev = torch.zeros(1, dtype=torch.int32, device=device)
+    out = torch.empty((cap, H), dtype=torch.bfloat16, device=device)
+
+    def device_m_call():
+        moe.moe_w4a16_fused_device_m(layer.dims, layer.prepared, layer.prepared_bytes, x, m_dev, ids, wts, k, emap,
+                                     cfg.num_global_experts, cap, layer.workspace, layer.workspace_bytes, out)
+
+    def case_at(m):
+        if m == ms[0]:
+            return base
+        if full:
+            return full_case(name, m, device, base.codes_dev)
+        i, w, em, rng = D.draw_routing(cfg, m, seed=cfg.index * 29 + 2 + m)
+        return Case(cfg, m, i, w, em, D.draw_activations_bf16(rng, m, H), base.codes)
+
+    def load(c):
+        m = c.m
+        x.fill_(1000.0)                       # junk past m: large, finite, routed to expert 0 with weight 5
+        ids.zero_()
+        wts.fill_(5.0)
+        if m:
+            x[:m].copy_(torch.from_numpy(c.xbits.view(np.int16)).view(torch.bfloat16))
+            ids[:m].copy_(torch.from_numpy(c.ids))
+            wts[:m].copy_(torch.from_numpy(c.w))
+        if emap is not None:
+            emap.copy_(torch.from_numpy(c.emap))
+        m_dev.fill_(m)
+
+    load(case_at(ms[0]))
+    device_m_call()                           # first call outside capture (one-time kernel attributes)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        device_m_call()
+    torch.cuda.synchronize()
+    for m in ms:
+        c = case_at(m)
+        load(c)
+        g.replay()
+        torch.cuda.synchronize()
+        got = bf16_tensor_to_f64(out)
+        assert np.all(got[m:] == 0), f"m={m}: rows past m not zero"
+        got = got[:m]
+        # eager reference at this m: the plain entry point on buffers of exactly m rows
+        ex = torch.from_numpy(c.xbits.view(np.int16)).view(torch.bfloat16).to(device)
+        ref_out = layer(ex, torch.from_numpy(c.ids).to(device), torch.from_numpy(c.w).to(device), expert_map=emap,
+                        num_global_experts=cfg.num_global_experts) if m else torch.empty((0, H), dtype=torch.bfloat16, device=device)
+        torch.cuda.synchronize()
+        eager = bf16_tensor_to_f64(ref_out)
+        decode_path = cap <= moe.MOE_DECODE_MAX_M
+        same = np.array_equal(got, eager)
+        print(f"  m={m}: replay == eager bit for bit: {same}", flush=True)
+        if not decode_path:
+            assert same, f"m={m}: graph replay differs from the eager call"
+        if m:
+            ok, err, bound = M.within_tolerance(got, oracle_out(c))
+            print(f"  m={m}: max|err| = {err:.3e}, bound = {bound:.3e}", flush=True)
+            assert ok, f"m={m}: {err} > {bound}"
+            ok, err, bound = M.within_tolerance(eager, oracle_out(c))
+            assert ok
+    del g, layer
+    torch.cuda.empty_cache()
