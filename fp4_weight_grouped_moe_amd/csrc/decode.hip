@@ -8,11 +8,13 @@
 // 128-bit loads in flight in a second register set while it dequantises the current one
 // in registers straight into MFMA A operands. Loop bounds are wave-uniform and loads are
 // unconditional (addresses clamped, contributions masked), so no load waits on a branch.
-//  * FC1: a workgroup (4 waves) owns one (route block, 16 or 32 FC1 columns) item at a
-//    time; its K blocks are dealt to the waves in slices, partial sums meet in LDS, and
+//  * FC1: one workgroup (8 waves) per CU owns one (route block, 16 or 32 FC1 columns) item
+//    at a time; its K blocks are dealt to the waves in slices, partial sums meet in LDS, and
 //    wave 0 applies the FC1 global scale, the activation, the router weight and the FC2
 //    global scale and stores the bf16 row slice of each route. The activation rows of
-//    all m tokens sit in LDS, staged by DMA.
+//    all m tokens sit in LDS, staged by DMA. (Two 4-wave workgroups per CU shared the CU's
+//    bandwidth unevenly: the older one streamed its items ~25% faster, so the younger ones
+//    set the launch's end.)
 //  * FC2 (K split): a workgroup owns a few hidden row groups and one pair of intermediate
 //    K blocks for every route block, with that K slice of every route staged in LDS; route
 //    results go into per-wave, per-token LDS sums (the top-k sum), and the last K split of
@@ -30,17 +32,19 @@ namespace moe {
 
 namespace {
 
-constexpr int kF1Threads = 256;
+constexpr int kF1Threads = 512;  // one 8-wave workgroup per CU (two 4-wave ones shared a CU unevenly)
 constexpr int kF1Waves = kF1Threads / 64;
 constexpr int kF1Slice = 4;          // K blocks per FC1 unit
 constexpr int kF2Threads = 1024;
 constexpr int kF2Waves = kF2Threads / 64;
 constexpr int kF2Slice = 2;          // K blocks per FC2 unit
-constexpr int kF1PackRoutes = 256;   // FC1 packs the routes itself up to this many (one per thread)
+constexpr int kF1PackRoutes = 256;   // FC1 packs the routes itself up to this many (one per thread of the first four waves)
 constexpr int kF1PackExperts = 2048; // and this many local experts (their counts share the partial-sum area)
 constexpr int kF1StaticLds = 2 * (kF1Waves - 1) * 2 * 64 * 16;   // the partial-sum area
 constexpr int kLdsPerCU = 163840;
-static_assert(kF1PackRoutes == kF1Threads, "one route per thread");
+static_assert(kF1PackRoutes <= kF1Threads, "one route per thread");
+// Rows + pack tables of the FC1 launch that packs its own routes (m <= 8 at hidden 4096)
+constexpr size_t kF1PackRowsBudget = 69632;
 
 // Route blocks the pack of R routes over E experts can produce: at most one per route, and
 // at most one per touched expert plus R / 16 more.
@@ -77,7 +81,7 @@ struct F1Unit {
 };
 
 template <int FMT, bool STAGED, bool PACK>
-__global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p) {
+__global__ __launch_bounds__(kF1Threads, 1) void decode_fc1_kernel(FusedParams p) {
   extern __shared__ __align__(16) uint8_t dyn[];
   // Partial sums of waves 1..3 for the item epilogue, double-buffered by item parity so that
   // one barrier per item suffices: a wave refills a buffer only after the next item's
@@ -133,6 +137,36 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
     if (F16 && !PACK && wave == 0) dma4(buffer_rsrc(p.xexp, uint32_t(p.m * 4)), sp, uint32_t(lane * 4));
   }
 
+  // The staged bf16 rows to f16 times 2^-p in place (NVFP4 with the routes packed here), one
+  // wave per row.
+  auto convert_rows = [&]() {
+    const int nch = xp / 8;
+    for (int t = wave; t < int(p.m); t += kF1Waves) {
+      u32x4* row = reinterpret_cast<u32x4*>(xs + t * xp);
+      float mx = 0.f;
+      for (int c = lane; c < nch; c += 64) {
+        const u32x4 v = row[c];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(v[i] << 16)), fabsf(__uint_as_float(v[i] & 0xFFFF0000u))));
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+      const int pe = (mx > 0.f && mx <= 3.4e38f) ? __builtin_amdgcn_frexp_expf(mx) - 15 : 0;
+      for (int c = lane; c < nch; c += 64) {
+        const u32x4 v = row[c];
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f16x2 h = f16x2{(_Float16)ldexpf(__uint_as_float(v[i] << 16), -pe),
+                                (_Float16)ldexpf(__uint_as_float(v[i] & 0xFFFF0000u), -pe)};
+          o[i] = __builtin_bit_cast(uint32_t, h);
+        }
+        row[c] = o;
+      }
+      if (lane == 0) sp[t] = pe;
+    }
+  };
   if constexpr (PACK) {
     // The route pack of these few routes (R <= 256, one per thread), done by every workgroup
     // in its own LDS so that no launch waits for another: local expert ids, counts, padded
@@ -172,7 +206,7 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
       }
     }
     pack_barrier();
-    const int l = sl[tid];
+    const int l = tid < kF1PackRoutes ? int(sl[tid]) : -1;
     if (l >= 0) atomicAdd(&cnt[l], 1);
     pack_barrier();
     constexpr int kPer = kF1PackExperts / kF1Threads;
@@ -286,36 +320,10 @@ __global__ __launch_bounds__(kF1Threads, 2) void decode_fc1_kernel(FusedParams p
   F1Unit ra, rb;
   issue(0, ra);
   issue(1, rb);
-  if constexpr (PACK && F16) {
-    // The bf16 rows (landed before the pack's last barrier) to f16 times 2^-p in place, one
-    // wave per row, while the first units' weights are in flight.
-    const int nch = xp / 8;
-    for (int t = wave; t < int(p.m); t += kF1Waves) {
-      u32x4* row = reinterpret_cast<u32x4*>(xs + t * xp);
-      float mx = 0.f;
-      for (int c = lane; c < nch; c += 64) {
-        const u32x4 v = row[c];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(v[i] << 16)), fabsf(__uint_as_float(v[i] & 0xFFFF0000u))));
-      }
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
-      const int pe = (mx > 0.f && mx <= 3.4e38f) ? __builtin_amdgcn_frexp_expf(mx) - 15 : 0;
-      for (int c = lane; c < nch; c += 64) {
-        const u32x4 v = row[c];
-        u32x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f16x2 h = f16x2{(_Float16)ldexpf(__uint_as_float(v[i] << 16), -pe),
-                                (_Float16)ldexpf(__uint_as_float(v[i] & 0xFFFF0000u), -pe)};
-          o[i] = __builtin_bit_cast(uint32_t, h);
-        }
-        row[c] = o;
-      }
-      if (lane == 0) sp[t] = pe;
-    }
-  }
+  // (the rows landed before the pack's last barrier; converted while the first units' weights
+  // are in flight)
+  if constexpr (PACK && F16) convert_rows();
+
   if constexpr (STAGED && !PACK) wait_vmcnt<0>();
   lds_barrier();
 
@@ -843,8 +851,7 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
   const int64_t items = p.cap_blocks * (g.n1_groups / 2);
   const bool pack = p.topk_ids != nullptr;                     // FC1 packs the routes (decode_fc1_packs)
   const size_t lds1 = size_t(p.m) * p.xs_pitch * 2 + 256 + (pack ? f1_pack_lds_bytes(int(p.m) * p.topk, g.E) : 0);
-  const bool two_per_cu = 2 * (lds1 + kF1StaticLds) <= size_t(kLdsPerCU);   // else the LDS holds one workgroup
-  const int64_t grid1 = max(int64_t(1), min(items, int64_t(num_cus) * (two_per_cu ? 2 : 1)));
+  const int64_t grid1 = max(int64_t(1), min(items, int64_t(num_cus)));   // one workgroup per CU
   if (pack)
     hipLaunchKernelGGL((decode_fc1_kernel<FMT, true, true>), dim3(grid1), dim3(kF1Threads), lds1, stream, p);
   else if (decode_stages_x(g, p.m))
@@ -885,13 +892,12 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
 }  // namespace
 
 bool decode_fc1_packs(const PreparedGeom& g, int64_t m, int topk) {
-  // Only while two FC1 workgroups still fit on a CU: with one (more staged rows) the
+  // Only up to about 64 KiB of staged rows (m <= 8 at hidden 4096): with more rows the
   // separate route-pack launch, which also converts the rows once, was measured faster
   // (small shape, m = 16: 127.8 against 129.1 us per layer).
   const int64_t routes = m * topk;
   return m >= 1 && routes <= kF1PackRoutes && g.E <= kF1PackExperts && decode_stages_x(g, m) &&
-         2 * (size_t(m) * decode_x_pitch(g) * 2 + 256 + f1_pack_lds_bytes(int(routes), g.E) + kF1StaticLds) <=
-             size_t(kLdsPerCU);
+         size_t(m) * decode_x_pitch(g) * 2 + 256 + f1_pack_lds_bytes(int(routes), g.E) <= kF1PackRowsBudget;
 }
 
 hipError_t launch_decode(const FusedParams& p, int num_cus, hipStream_t stream, LaunchMarks* marks) {

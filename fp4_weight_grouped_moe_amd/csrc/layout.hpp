@@ -97,7 +97,7 @@ __host__ __device__ inline PackGeom make_pack_geom(int64_t cap, int64_t k, int64
 }
 
 constexpr int kDecodeMaxM = 16;          // token columns of the decode path
-constexpr int kDecodeStageBytes = 147456; // LDS for the decode FC1 staged activation rows (144 KiB)
+constexpr int kDecodeStageBytes = 131072; // LDS for the decode FC1 staged activation rows (128 KiB)
 
 // Decode FC1 keeps the activation rows in LDS when they fit, at a pitch of hp rounded up to
 // 512 elements (whole 1 KiB rows of LDS DMA); up to 64 KiB of rows two workgroups share a
