@@ -342,14 +342,20 @@ __global__ __launch_bounds__(kF1Threads, 1) void decode_fc1_kernel(FusedParams p
       const int kb = sl * kF1Slice + j;
       if (kb < kb1) {
         float sa[4], sb[4];
-        decode_scales<FMT>(r.s0[j], sa);
-        decode_scales<FMT>(r.s1[j], sb);
+        NvScalesF16 ha, hb;
+        if constexpr (F16) {
+          ha = nv_scales_f16(r.s0[j]);
+          hb = nv_scales_f16(r.s1[j]);
+        } else {
+          decode_scales<FMT>(r.s0[j], sa);
+          decode_scales<FMT>(r.s1[j], sb);
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           if constexpr (F16) {
             const f16x8 xb = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(xs + xoff[s] + kb * kKBlock));
-            acc0 = mfma16h(dq8_nv_f16(r.q0[j][s], split_nv_scale(sa[s])), xb, acc0);
-            acc1 = mfma16h(dq8_nv_f16(r.q1[j][s], split_nv_scale(sb[s])), xb, acc1);
+            acc0 = mfma16h(dq8_nv_f16(r.q0[j][s], ha.step(s)), xb, acc0);
+            acc1 = mfma16h(dq8_nv_f16(r.q1[j][s], hb.step(s)), xb, acc1);
           } else {
             bf16x8 xb;
             if (STAGED) xb = load_bf16x8(xs + xoff[s] + kb * kKBlock);
@@ -751,14 +757,18 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
     for (int j = 0; j < kF3KB; ++j) {
       if (kq0 + j < kb2) {
         float sc[RG][4];
+        NvScalesF16 sh[RG];
 #pragma unroll
-        for (int rr = 0; rr < RG; ++rr) decode_scales<FMT>(r.s[rr][j], sc[rr]);
+        for (int rr = 0; rr < RG; ++rr) {
+          if constexpr (F16) sh[rr] = nv_scales_f16(r.s[rr][j]);
+          else decode_scales<FMT>(r.s[rr][j], sc[rr]);
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           if constexpr (F16) {
             const f16x8 b = route >= 0 ? *reinterpret_cast<const f16x8*>(brow + j * kKBlock * 2 + s * 64) : zero_f16x8();
 #pragma unroll
-            for (int rr = 0; rr < RG; ++rr) acc[rr] = mfma16h(dq8_nv_f16(r.q[rr][j][s], split_nv_scale(sc[rr][s])), b, acc[rr]);
+            for (int rr = 0; rr < RG; ++rr) acc[rr] = mfma16h(dq8_nv_f16(r.q[rr][j][s], sh[rr].step(s)), b, acc[rr]);
           } else {
             const bf16x8 b = route >= 0 ? *reinterpret_cast<const bf16x8*>(brow + j * kKBlock * 2 + s * 64) : zero_bf16x8();
 #pragma unroll

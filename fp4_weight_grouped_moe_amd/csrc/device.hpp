@@ -90,28 +90,30 @@ __device__ __forceinline__ bf16x8 dq8<1>(uint32_t q, float scale) { return dq8_s
 template <>
 __device__ __forceinline__ bf16x8 dq8<2>(uint32_t q, float scale) { return dq8_pow2(q, scale); }
 
-// NVFP4 to f16: an E4M3 scale s = 2^e * m with m in [1, 2) (sign kept with m). The scaled
-// convert applies 2^e; one packed f16 multiply applies m. Every E2M1 x E4M3 product lies in
-// [2^-10, 2880] with at most 6 significant bits, so the f16 result is exact -- at half the
-// VALU work of the f32 route.
-struct NvScaleF16 {
-  float pow2;
-  f16x2 mant;
+// NVFP4 to f16. The four E4M3 scale bytes of a K block (byte s = the scale of MFMA step s)
+// decode exactly to f16 (every E4M3 value, subnormals, sign and NaN included, is an f16
+// value), two per hardware FP8 convert: pair 0 holds steps 0 and 1, pair 1 steps 2 and 3.
+struct NvScalesF16 {
+  f16x2 p[2];
+  __device__ __forceinline__ _Float16 step(int s) const { return p[s >> 1][s & 1]; }
 };
-__device__ __forceinline__ NvScaleF16 split_nv_scale(float s) {
-  const uint32_t b = __float_as_uint(s);
-  NvScaleF16 r;
-  r.pow2 = __uint_as_float(b & 0x7F800000u);
-  const _Float16 m = (_Float16)__uint_as_float((b & 0x807FFFFFu) | 0x3F800000u);
-  r.mant = f16x2{m, m};
+__device__ __forceinline__ NvScalesF16 nv_scales_f16(uint32_t w) {
+  NvScalesF16 r;
+  r.p[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  r.p[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
   return r;
 }
-__device__ __forceinline__ f16x8 dq8_nv_f16(uint32_t q, const NvScaleF16& sc) {
+// 8 E2M1 codes times one E4M3 scale (as f16) -> 8 f16: the FP4 convert gives the E2M1 values,
+// one packed multiply (the scale taken from one half of its register) applies the scale. Every
+// E2M1 x E4M3 product lies in [2^-10, 2688] with at most 6 significant bits, so the f16
+// result is exact -- at half the VALU work of the f32 route.
+__device__ __forceinline__ f16x8 dq8_nv_f16(uint32_t q, _Float16 scale) {
+  const f16x2 m = {scale, scale};
   f16x2 v[4];
-  v[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc.pow2, 0) * sc.mant;
-  v[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc.pow2, 1) * sc.mant;
-  v[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc.pow2, 2) * sc.mant;
-  v[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sc.pow2, 3) * sc.mant;
+  v[0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 0) * m;
+  v[1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 1) * m;
+  v[2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 2) * m;
+  v[3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, 1.0f, 3) * m;
   return __builtin_bit_cast(f16x8, v);
 }
 

@@ -74,10 +74,11 @@ struct GemmCtx {
 };
 
 // Dequantisation of one wave's fragment dword for MFMA step s, for the three routes:
-// NVFP4 to f16 (pow2 by the scaled convert, mantissa by one packed f16 multiply), NVFP4 to
+// NVFP4 to f16 (the FP4 convert, then one packed f16 multiply by the scale), NVFP4 to
 // bf16 through f32, MXFP4 to bf16 (the scaled convert alone).
-// Each keeps the raw scale dword and decodes the scale of step s on use (fewer live
-// registers than four decoded scales).
+// The bf16 routes keep the raw scale dword and decode the scale of step s on use (fewer live
+// registers than four decoded scales); the f16 route decodes the four scales at once, two per
+// convert.
 template <int FMT, bool F16>
 struct Deq {
   typedef bf16x8 T;
@@ -94,12 +95,9 @@ struct Deq {
 template <>
 struct Deq<FMT_NVFP4, true> {
   typedef f16x8 T;
-  uint32_t w;
-  __device__ __forceinline__ void set(uint32_t v) { w = v; }
-  __device__ __forceinline__ T operator()(uint32_t q, int s) const {
-    const f32x2 pr = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s >= 2 ? w >> 16 : w, 1.0f, false);
-    return dq8_nv_f16(q, split_nv_scale(pr[s & 1]));
-  }
+  NvScalesF16 sc;
+  __device__ __forceinline__ void set(uint32_t v) { sc = nv_scales_f16(v); }
+  __device__ __forceinline__ T operator()(uint32_t q, int s) const { return dq8_nv_f16(q, sc.step(s)); }
 };
 
 __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, const f32x4& c) { return mfma16(a, b, c); }
