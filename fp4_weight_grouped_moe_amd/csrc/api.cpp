@@ -370,9 +370,9 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   fp.cap_blocks = pg.cap_blocks;
   fp.w4a8 = w4a8 ? 1 : 0;
   fp.atomic_bf16 = atomic_bf16 && !decode ? 1 : 0;
-  fp.inter32 = w4a8 ? reinterpret_cast<float*>(ws + fg.off_inter32) : nullptr;
-  fp.inter8 = w4a8 && decode ? ws + fg.off_inter8 : nullptr;
-  fp.sc8 = w4a8 && decode ? ws + fg.off_sc8 : nullptr;
+  fp.inter32 = w4a8 && decode ? reinterpret_cast<float*>(ws + fg.off_inter32) : nullptr;
+  fp.inter8 = w4a8 ? ws + fg.off_inter8 : nullptr;
+  fp.sc8 = w4a8 ? ws + fg.off_sc8 : nullptr;
   fp.topk_weights = topk_weights;
   if (fc1_packs) {
     fp.topk_ids = topk_ids;

@@ -588,8 +588,6 @@ __host__ __device__ inline size_t f8_lds_bytes(int64_t m, int64_t topk, int64_t 
          f3_exp_bytes(m * topk) + size_t(kF3Waves) * m * 16 * RG * 4;
 }
 
-typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
-
 template <int FMT, int RG, bool W8>
 __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedParams p) {
   static_assert(!W8 || kF3KB == 2, "the block-scaled FC2 takes one 128-K block pair (256 codes) per workgroup");

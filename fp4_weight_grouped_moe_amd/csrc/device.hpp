@@ -13,6 +13,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 // D += A * B for a 16x16x32 bf16 step. Lane l holds A[l%16][8*(l/16) + j] and
 // B[8*(l/16) + j][l%16] (j = 0..7); D row 4*(l/16) + i, column l%16 in element i.
@@ -198,6 +199,65 @@ __device__ __forceinline__ float silu_f32(float z) {
   // z * sigmoid(z) with the hardware exp2 and reciprocal; the oracle uses exact exp and the
   // bf16 tolerance absorbs the few-ulp difference.
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// MXFP8 (OCP MX v1.0 with OCP FP8 E4M3FN elements, one E8M0 scale per 32 along K), the W4A8
+// variant's FC2 operand. Scale 2^e with e = ceil(log2(amax / 448)) clamped to [-127, 127], so
+// the largest element lands in (224, 448] and nothing saturates; codes round to nearest, ties
+// to even; an all-zero group stores scale byte 0 and zero codes.
+
+// e for a group maximum amax > 0, exactly: amax = fr 2^ex with fr in [0.5, 1), so amax / 448 =
+// (fr / 0.875) 2^(ex - 9) with fr / 0.875 in [0.57, 1.15), above 1 only for fr > 0.875.
+__device__ __forceinline__ int mx8_exponent(float amax) {
+  const int ex = __builtin_amdgcn_frexp_expf(amax);
+  const float fr = __builtin_amdgcn_frexp_mantf(amax);
+  const int e = ex - 9 + (fr > 0.875f ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Round |s| <= 448 to the nearest E4M3FN value, ties to even: 3 fraction bits from 2^-6 up
+// (the normal range), multiples of 2^-9 below it (the subnormal range).
+__device__ __forceinline__ float e4m3_rne(float s) {
+  const float a = fabsf(s);
+  float q;
+  if (a >= 0.015625f) {
+    const uint32_t b = __float_as_uint(a);
+    q = __uint_as_float((b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u);
+  } else {
+    q = __builtin_rintf(a * 512.f) * (1.f / 512.f);
+  }
+  return copysignf(q, s);
+}
+
+// The E4M3FN code of a value q that is already on the grid (|q| <= 448).
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+  const uint32_t b = __float_as_uint(q), sign = (b >> 24) & 0x80u;
+  const float a = fabsf(q);
+  if (a >= 0.015625f) return sign | ((((b >> 23) & 0xFFu) - 120u) << 3) | ((b >> 20) & 7u);   // biased 127 -> 7
+  return sign | uint32_t(a * 512.f);                                                          // subnormal: multiples of 2^-9
+}
+
+// Four values of one group (scale exponent e, group maximum amax) -> four E4M3 codes, value i
+// in byte i.
+__device__ __forceinline__ uint32_t mx8_codes4(const float* v, int e, float amax) {
+  uint32_t w = 0u;
+  if (amax > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w |= e4m3_code(e4m3_rne(ldexpf(v[i], -e))) << (8 * i);
+  }
+  return w;
+}
+
+// 4 x 4 transpose of one dword per lane quarter (lanes 16 q .. 16 q + 15): afterwards lane
+// (c, q) holds in dword t what lane (c, t) held in dword q. Two rounds of gfx950 lane swaps:
+// quarters {0,1} <-> {2,3} between dwords (0, 2) and (1, 3), then quarters 1 <-> 0 and 3 <-> 2
+// between dwords (0, 1) and (2, 3).
+__device__ __forceinline__ u32x4 transpose_quarters(const u32x4& d) {
+  const auto a = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto e = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  return u32x4{c[0], c[1], e[0], e[1]};
 }
 
 }  // namespace moe

@@ -34,6 +34,7 @@ constexpr int kGemmThreads = 512;                       // 8 waves, two per SIMD
 constexpr int kRowBytes = kKBlock * 2;                  // one activation row of a K block: 256 B
 constexpr int kBlockBytes = kBlockM * kRowBytes;        // one route block of a K block: 4 KiB
 constexpr int kLdsBytes = 131072;                       // the activation stage ring
+constexpr int kW8AmaxOffset = 98304;                    // W4A8 FC1 epilogue: per-wave group maxima (4 KiB)
 
 // Wave layout and pipeline depth for tiles of NB route blocks: the 8 waves split the N tile,
 // 2 row groups x NB blocks each, so every fragment is loaded and dequantised by exactly one
@@ -269,6 +270,74 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
   // Epilogue. Lane (r0 = 4 (lane / 16), col = lane % 16) holds rows r0..r0+3 of each
   // 16-row group, route column col of each block.
   const int r0 = 4 * (lane >> 4), col = lane & 15;
+  if constexpr (PHASE == 1 && FMT == FMT_MXFP4) {
+    if (p.w4a8) {
+      // W4A8: the activation output (without the router weight, which FC2 applies) rounded to
+      // MXFP8 right here -- E4M3 codes into the route slot's code row, one E8M0 byte per 32
+      // columns. With SiLU-SwiGLU a wave holds 16 columns of each route (one gate/up pair) and
+      // the other half of their MX block sits in the neighbouring wave: the two exchange their
+      // halves' maxima through LDS. With relu2 a wave's two row groups are one whole block.
+      static_assert(P::kDepth * P::kStage <= kW8AmaxOffset, "the exchange area lies past the stage ring");
+      const float g13 = p.g13[e];
+      const bool swiglu = g.act == ACT_SWIGLU;
+      float v[BW][FR][4], am[BW];
+#pragma unroll
+      for (int bb = 0; bb < BW; ++bb) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (swiglu) {
+            v[bb][0][i] = silu_f32(acc[0][bb][i] * g13) * (acc[1][bb][i] * g13);
+            v[bb][1][i] = 0.f;
+          } else {
+#pragma unroll
+            for (int f = 0; f < FR; ++f) {
+              const float u = fmaxf(acc[f][bb][i] * g13, 0.f);
+              v[bb][f][i] = u * u;
+            }
+          }
+#pragma unroll
+          for (int f = 0; f < FR; ++f) a = fmaxf(a, fabsf(v[bb][f][i]));
+        }
+        a = fmaxf(a, __shfl_xor(a, 16, 64));
+        am[bb] = fmaxf(a, __shfl_xor(a, 32, 64));
+      }
+      if (swiglu) {
+        float* xam = reinterpret_cast<float*>(lds + kW8AmaxOffset);      // [waves][BW][16]
+        if (lane < 16) {
+#pragma unroll
+          for (int bb = 0; bb < BW; ++bb) xam[(wave * BW + bb) * 16 + col] = am[bb];
+        }
+        lds_barrier();
+#pragma unroll
+        for (int bb = 0; bb < BW; ++bb) am[bb] = fmaxf(am[bb], xam[((wave ^ 1) * BW + bb) * 16 + col]);
+      }
+      const int64_t ip = g.ip;
+#pragma unroll
+      for (int bb = 0; bb < BW; ++bb) {
+        if (bb < nb && rg_base < c.groups) {
+          const int64_t slot = (fb + bb) * kBlockM + col;
+          if (p.slot_info[slot].x >= 0) {
+            const float amax = am[bb];
+            const int ex = amax > 0.f ? mx8_exponent(amax) : 0;
+            const uint8_t sbyte = uint8_t(amax > 0.f ? ex + 127 : 0);
+            uint8_t* crow = p.inter8 + slot * ip;
+            if (swiglu) {
+              const int64_t icol = int64_t(rg_base >> 1) * 16 + r0;
+              *reinterpret_cast<uint32_t*>(crow + icol) = mx8_codes4(v[bb][0], ex, amax);
+              if ((wave & 1) == 0 && r0 == 0) p.sc8[slot * (ip / 32) + icol / 32] = sbyte;
+            } else {
+#pragma unroll
+              for (int f = 0; f < FR; ++f)
+                *reinterpret_cast<uint32_t*>(crow + int64_t(rg_base + f) * 16 + r0) = mx8_codes4(v[bb][f], ex, amax);
+              if (r0 == 0) p.sc8[slot * (ip / 32) + rg_base / 2] = sbyte;
+            }
+          }
+        }
+      }
+      return;
+    }
+  }
   if (PHASE == 1) {
     const float g13 = p.g13[e], g2 = p.g2[e];
 #pragma unroll
@@ -351,7 +420,181 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
   }
 }
 
-template <int FMT, int PHASE>
+// W4A8 FC2: the block-scaled FP4 x FP8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4), one per
+// (row group, route block, K block), E8M0 scales applied by the matrix core -- no
+// dequantisation. Operand lanes: A (weights) lane (c, q) holds the 32 consecutive K of MX block
+// q of row c, made from the prepared fragment (8-K chunks dealt over the lane quarters) by a
+// 4 x 4 dword transpose across the quarters; B (the routes' MXFP8 codes, written by FC1) lane
+// (c, q) holds K 16 q .. +15 and 64 + 16 q .. +15 of route c; each lane passes the scale byte
+// of MX block q of its row or route. The activation codes of a K block (128 B per route, the
+// 16-byte chunk j of route row r at position j ^ (r % 8): the 16 lanes reading one chunk column
+// hit distinct banks) and their scale dwords stream through the LDS stage ring as in the
+// W4A16 item; each wave's fragments and scale dwords through its register ring.
+template <int NB>
+struct PlanW8 {
+  static constexpr int FR = 2;                                       // row groups per wave
+  static constexpr int XD = NB >= 4 ? NB / 4 : 1;                    // 1 KiB code loads per wave and stage
+  static constexpr int kCodes = NB * kBlockM * kKBlock;              // codes of a stage
+  static constexpr int kStage = kCodes + 512;                        // + up to 128 routes' scale dwords
+  static constexpr int kDepth = NB >= 4 ? 3 : 5;   // (deeper rings spill registers)
+  static constexpr int kLds = XD + 1;                                // loads into LDS per wave and stage
+  static constexpr int kLoads = kLds + 2 * FR;
+  static_assert(kDepth >= 3 && (kDepth - 1) * kLoads < 64, "ring too shallow or vmcnt out of range");
+  static_assert(kLds <= 2 * FR, "the stage wait relies on at least as many register loads as LDS loads");
+  static_assert(kDepth * kStage <= kLdsBytes, "stage ring larger than the LDS");
+};
+
+template <int NB>
+__device__ __forceinline__ void gemm_item_w8(const FusedParams& p, const GemmCtx& c, uint8_t* lds, int mt, int nt) {
+  using P = PlanW8<NB>;
+  constexpr int D = P::kDepth, FR = P::FR, XD = P::XD;
+  const PreparedGeom& g = p.g;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4, col = lane & 15;
+  const int2 tile = p.tiles[mt];
+  const int64_t fb = tile.x;
+  const int nb = __builtin_amdgcn_readfirstlane(tile.y & 0xFF);
+  const int e = __builtin_amdgcn_readfirstlane(tile.y >> 8);
+  const int kbs = c.kbs;
+  const int ip = int(g.ip);
+
+  // Code loads: load j of this wave brings routes 8 qd .. 8 qd + 7 of the tile (qd below; with
+  // fewer than 4 blocks several waves repeat the same load into the same place), lane i route
+  // 8 qd + i / 8, stored chunk i % 8 = source chunk (i % 8) ^ (route % 8). Routes past the
+  // tile's blocks read 0. Scale load: routes 64 h + lane, dword K block kb of the route's scale
+  // row.
+  uint32_t coff[XD];
+  int cdst[XD];
+#pragma unroll
+  for (int j = 0; j < XD; ++j) {
+    const int qd = NB >= 4 ? wave * XD + j : (wave % (2 * NB));
+    const int row = 8 * qd + (lane >> 3);
+    const uint32_t chunk = uint32_t((lane & 7) ^ (row & 7));
+    cdst[j] = qd * 1024;
+    coff[j] = row < nb * kBlockM ? uint32_t((fb * kBlockM + row) * ip) + chunk * 16 : kOutOfRange;
+  }
+  const int h = NB == 8 ? (wave & 1) : 0;
+  const int srow = 64 * h + lane;
+  const uint32_t soff = srow < nb * kBlockM ? uint32_t((fb * kBlockM + srow) * (ip / 32)) : kOutOfRange;
+  const __amdgpu_buffer_rsrc_t cres = buffer_rsrc(p.inter8, uint32_t(p.cap_blocks * kBlockM * ip));
+  const __amdgpu_buffer_rsrc_t bsres = buffer_rsrc(p.sc8, uint32_t(p.cap_blocks * kBlockM * (ip / 32)));
+
+  const int tile_groups = min(16, c.groups - nt * 16);
+  const int64_t g0 = int64_t(e) * c.groups + nt * 16;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(c.nib + g0 * kbs * kFragBytes), 0,
+      __builtin_amdgcn_readfirstlane(tile_groups * kbs * kFragBytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      uniform_ptr(c.scb + g0 * c.sc_per_group), 0,
+      __builtin_amdgcn_readfirstlane(int(tile_groups * c.sc_per_group)), 0x00020000);
+  const int rg_base = nt * 16 + wave * FR;
+  const int sc_lane = col * 16;
+
+  u32x4 wr[D][FR];
+  uint32_t sc[D][FR];
+  // One stage (K block kb, clamped for the weights; stages past K are issued and never used):
+  // scale dwords and fragments into registers, then codes and scale dwords into LDS.
+  auto issue = [&](int kb, int slot, u32x4* wd, uint32_t* scd) {
+    uint8_t* st = lds + slot * P::kStage;
+    const int kc = min(kb, kbs - 1);
+#pragma unroll
+    for (int f = 0; f < FR; ++f)
+      scd[f] = __builtin_amdgcn_raw_buffer_load_b32(
+          sres, int((wave * FR + f) * c.sc_per_group + (kc >> 2) * g.sc_chunk_bytes) + sc_lane + (kc & 3) * 4, 0, 0);
+#pragma unroll
+    for (int f = 0; f < FR; ++f)
+      wd[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          wres, ((wave * FR + f) * kbs + kc) * kFragBytes + lane * 16, 0, 0));
+#pragma unroll
+    for (int j = 0; j < XD; ++j) dma16(cres, st + cdst[j], coff[j] + uint32_t(kc) * kKBlock);
+    dma4(bsres, st + P::kCodes + 256 * h, soff + uint32_t(kc) * 4);
+    __builtin_amdgcn_sched_barrier(0);            // stages leave in order
+  };
+
+  f32x4 acc[FR][NB];
+#pragma unroll
+  for (int f = 0; f < FR; ++f)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // lane (col, q): route col of each block, chunks q and q + 4 of its row (swizzled)
+  const int olo = col * kKBlock + ((q ^ (col & 7)) << 4);
+  const int ohi = olo ^ 64;
+  auto compute = [&](int slot, const u32x4* wq, const uint32_t* scd) {
+    const uint8_t* st = lds + slot * P::kStage;
+    i32x8 a[FR];
+    int sa[FR];
+#pragma unroll
+    for (int f = 0; f < FR; ++f) {
+      const u32x4 t = transpose_quarters(wq[f]);
+      a[f] = i32x8{int(t[0]), int(t[1]), int(t[2]), int(t[3]), 0, 0, 0, 0};
+      sa[f] = int(scd[f] >> (8 * q));
+    }
+    // B operands one block ahead of the MFMAs (two register sets; the scheduling barriers keep
+    // the compiler from hoisting every block's reads)
+    auto bread = [&](int b, i32x8& bop, uint32_t& sbw) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + (b * kBlockM + col) * kKBlock + (olo - col * kKBlock));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(st + (b * kBlockM + col) * kKBlock + (ohi - col * kKBlock));
+      bop = i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+      sbw = *reinterpret_cast<const uint32_t*>(st + P::kCodes + 4 * (b * kBlockM + col));
+    };
+    i32x8 bop[2];
+    uint32_t sbw[2];
+    bread(0, bop[0], sbw[0]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b + 1 < NB) bread(b + 1, bop[(b + 1) & 1], sbw[(b + 1) & 1]);
+      const int sb = int(sbw[b & 1] >> (8 * q));
+#pragma unroll
+      for (int f = 0; f < FR; ++f)
+        acc[f][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[f], bop[b & 1], acc[f][b], 4, 0, 0, sa[f], 0, sb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // The same ring as the W4A16 item (loads into LDS and into registers complete in order within
+  // each kind): the wait leaves only the later stages' LDS loads outstanding.
+  auto step = [&](int kb, int j) {
+    wait_vmcnt<(D - 2) * P::kLds>();
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int jn = (j + D - 1) % D;
+    issue(kb + D - 1, jn, wr[jn], sc[jn]);
+    compute(j, wr[j], sc[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) issue(j, j, wr[j], sc[j]);
+  int kb = 0;
+  for (; kb + D <= kbs; kb += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) step(kb + j, j);
+  }
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j)
+    if (kb + j < kbs) step(kb + j, j);
+  wait_vmcnt<0>();
+
+  // Epilogue: the weighted fp32 row of each route (router weight x FC2 global scale, outside
+  // the quantisation), summed over top-k by the combine pass.
+  const int r0 = 4 * q;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    if (b < nb) {
+      const int r = p.sorted_route_ids[(fb + b) * kBlockM + col];
+      if (r >= 0) {
+        const float wt = __int_as_float(p.slot_info[(fb + b) * kBlockM + col].y) * p.g2[e];
+#pragma unroll
+        for (int f = 0; f < FR; ++f) {
+          const int64_t hh = int64_t(rg_base + f) * 16 + r0;
+          if (hh < g.H) *reinterpret_cast<f32x4*>(p.y + int64_t(r) * g.H + hh) = acc[f][b] * wt;
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, int PHASE, bool W8>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
   extern __shared__ __align__(16) uint8_t lds[];
   const PreparedGeom& g = p.g;
@@ -429,10 +672,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
     const int mt = item / n_nt, nt = item % n_nt;
     const int nb = __builtin_amdgcn_readfirstlane(p.tiles[mt].y & 0xFF);
     // Tiles are compiled for 1, 2, 4 or 8 route blocks so that the MFMA loop is straight-line.
-    if (nb <= 1) gemm_item<FMT, PHASE, 1>(p, c, lds, mt, nt);
-    else if (nb <= 2) gemm_item<FMT, PHASE, 2>(p, c, lds, mt, nt);
-    else if (nb <= 4) gemm_item<FMT, PHASE, 4>(p, c, lds, mt, nt);
-    else gemm_item<FMT, PHASE, 8>(p, c, lds, mt, nt);
+    if constexpr (W8) {
+      if (nb <= 1) gemm_item_w8<1>(p, c, lds, mt, nt);
+      else if (nb <= 2) gemm_item_w8<2>(p, c, lds, mt, nt);
+      else if (nb <= 4) gemm_item_w8<4>(p, c, lds, mt, nt);
+      else gemm_item_w8<8>(p, c, lds, mt, nt);
+    } else {
+      if (nb <= 1) gemm_item<FMT, PHASE, 1>(p, c, lds, mt, nt);
+      else if (nb <= 2) gemm_item<FMT, PHASE, 2>(p, c, lds, mt, nt);
+      else if (nb <= 4) gemm_item<FMT, PHASE, 4>(p, c, lds, mt, nt);
+      else gemm_item<FMT, PHASE, 8>(p, c, lds, mt, nt);
+    }
   }
 }
 
@@ -453,10 +703,10 @@ __global__ void combine_kernel(const float* __restrict__ y, const int32_t* __res
 
 }  // namespace
 
-template <int FMT, int PHASE>
+template <int FMT, int PHASE, bool W8>
 hipError_t allow_large_lds(size_t lds) {
   // The stage ring needs more than the 64 KiB default of dynamic LDS.
-  static hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<FMT, PHASE>),
+  static hipError_t once = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<FMT, PHASE, W8>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   return once;
 }
@@ -465,19 +715,21 @@ hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, La
   // One 8-wave workgroup per CU (two waves per SIMD, up to 256 registers each).
   const int grid = num_cus;
   const size_t lds = kLdsBytes;
-  hipError_t e = p.g.fmt == FMT_NVFP4 ? allow_large_lds<FMT_NVFP4, 1>(lds) : allow_large_lds<FMT_MXFP4, 1>(lds);
-  if (e == hipSuccess) e = p.g.fmt == FMT_NVFP4 ? allow_large_lds<FMT_NVFP4, 2>(lds) : allow_large_lds<FMT_MXFP4, 2>(lds);
-  if (e != hipSuccess) return e;
   const bool nv = p.g.fmt == FMT_NVFP4;
-  if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 1>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
-  else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 1>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
+  // W4A8 (MXFP4 weights only): FC1 rounds its activation output to MXFP8 codes in its epilogue
+  // and FC2 runs the block-scaled MFMA on them.
+  const bool w8 = !nv && p.w4a8;
+  hipError_t e = nv ? allow_large_lds<FMT_NVFP4, 1, false>(lds) : allow_large_lds<FMT_MXFP4, 1, false>(lds);
+  if (e == hipSuccess)
+    e = nv ? allow_large_lds<FMT_NVFP4, 2, false>(lds)
+           : (w8 ? allow_large_lds<FMT_MXFP4, 2, true>(lds) : allow_large_lds<FMT_MXFP4, 2, false>(lds));
+  if (e != hipSuccess) return e;
+  if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 1, false>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
+  else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 1, false>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   if (marks) marks->after(stream, KID_FC1);
-  if (p.w4a8) {
-    if (hipError_t e2 = launch_mxfp8_requant(p, false, stream); e2 != hipSuccess) return e2;
-    if (marks) marks->after(stream, KID_REQUANT);
-  }
-  if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
-  else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 2>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
+  if (nv) hipLaunchKernelGGL((gemm_kernel<FMT_NVFP4, 2, false>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
+  else if (w8) hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 2, true>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
+  else hipLaunchKernelGGL((gemm_kernel<FMT_MXFP4, 2, false>), dim3(grid), dim3(kGemmThreads), lds, stream, p);
   if (marks) marks->after(stream, KID_FC2);
   if (!p.atomic_bf16) {
     launch_combine(p, stream);

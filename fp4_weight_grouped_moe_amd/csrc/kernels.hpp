@@ -74,15 +74,15 @@ struct FusedParams {
   const float* topk_weights;     // [m * topk]
   const int32_t* expert_map;     // [num_global_experts] or null
   int32_t num_global_experts;
-  // W4A8 variant: FC1 stores the activation output without the router weight, the output
-  // rows are rounded to MXFP8 in place (launch_mxfp8_requant), and FC2 applies router weight x
-  // FC2 global scale per route.
+  // W4A8 variant: the activation output (without the router weight) rounded to MXFP8 codes and
+  // E8M0 scales -- by the grouped GEMM's FC1 epilogue, on the decode path from FC1's fp32 rows --
+  // and FC2 on the block-scaled MFMA, applying router weight x FC2 global scale per route.
   int32_t w4a8;
   // Grouped-GEMM path, opt-in: FC2 adds each route's weighted row into the bf16 output with
   // packed-bf16 atomics (FC1 zeroes the output first); no fp32 rows, no combine pass.
   int32_t atomic_bf16;
-  float* inter32;                // W4A8: fp32 [cap_routes, ip] activation output of FC1
-  uint8_t* inter8;               // W4A8, decode path: MXFP8 codes [cap_routes, ip] (E4M3)
+  float* inter32;                // W4A8, decode path: fp32 [cap_routes, ip] activation output of FC1
+  uint8_t* inter8;               // W4A8: MXFP8 codes [cap_routes, ip] (E4M3)
   uint8_t* sc8;                  //   and their E8M0 scales [cap_routes, ip / 32]
   uint16_t* inter;               // bf16 [cap_routes, ip]
   const uint16_t* x16;           // f16 [m, H] scaled activations (NVFP4 f16 MFMA route)

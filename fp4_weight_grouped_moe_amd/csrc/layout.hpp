@@ -121,10 +121,12 @@ __host__ __device__ inline FusedGeom make_fused_geom(const PreparedGeom& w, int6
   size_t o = 0;
   f.off_pack = o;  o = align256(o + f.pack.total);
   f.off_inter = o; o = align256(o + size_t(f.pack.cap_routes) * w.ip * 2);
-  // W4A8 (MXFP4 weights): the fp32 activation output, rounded to MXFP8 into the bf16 rows above
-  f.off_inter32 = o; o = align256(o + (w.fmt == FMT_MXFP4 ? size_t(f.pack.cap_routes) * w.ip * 4 : 0));
-  // W4A8 on the decode path: the MXFP8 codes and E8M0 scale bytes themselves (block-scaled FC2)
-  const bool w8 = w.fmt == FMT_MXFP4 && cap <= kDecodeMaxM;
+  // W4A8 (MXFP4 weights) on the decode path: FC1's fp32 activation output, rounded to MXFP8
+  // after FC1
+  const bool dec = cap <= kDecodeMaxM;
+  f.off_inter32 = o; o = align256(o + (w.fmt == FMT_MXFP4 && dec ? size_t(f.pack.cap_routes) * w.ip * 4 : 0));
+  // W4A8: the MXFP8 codes and E8M0 scale bytes that the block-scaled FC2 multiplies
+  const bool w8 = w.fmt == FMT_MXFP4;
   f.off_inter8 = o; o = align256(o + (w8 ? size_t(f.pack.cap_routes) * w.ip : 0));
   f.off_sc8 = o;    o = align256(o + (w8 ? size_t(f.pack.cap_routes) * (w.ip / 32) : 0));
   f.off_x16 = o;   o = align256(o + size_t(cap) * w.H * 2);

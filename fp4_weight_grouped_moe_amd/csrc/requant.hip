@@ -22,31 +22,9 @@ namespace {
 
 constexpr int kRequantThreads = 256;
 
-// Round |s| <= 448 to the nearest E4M3FN value, ties to even: 3 fraction bits from 2^-6 up
-// (the normal range), multiples of 2^-9 below it (the subnormal range).
-__device__ __forceinline__ float e4m3_rne(float s) {
-  const float a = fabsf(s);
-  float q;
-  if (a >= 0.015625f) {
-    const uint32_t b = __float_as_uint(a);
-    q = __uint_as_float((b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u);
-  } else {
-    q = __builtin_rintf(a * 512.f) * (1.f / 512.f);
-  }
-  return copysignf(q, s);
-}
-
-// Lane l of a wave holds columns 8 l .. 8 l + 7 of a 512-column slice (fp32 in, bf16 out);
-// lanes 4 g .. 4 g + 3
-// hold MX group g of the slice, so the group maximum is two xor shuffles.
-// The E4M3FN code of a value q that is already on the grid (|q| <= 448).
-__device__ __forceinline__ uint32_t e4m3_code(float q) {
-  const uint32_t b = __float_as_uint(q), sign = (b >> 24) & 0x80u;
-  const float a = fabsf(q);
-  if (a >= 0.015625f) return sign | ((((b >> 23) & 0xFFu) - 120u) << 3) | ((b >> 20) & 7u);   // biased 127 -> 7
-  return sign | uint32_t(a * 512.f);                                                          // subnormal: multiples of 2^-9
-}
-
+// Lane l of a wave holds columns 8 l .. 8 l + 7 of a 512-column slice (fp32 in, bf16 or codes
+// out); lanes 4 g .. 4 g + 3 hold MX group g of the slice, so the group maximum is two xor
+// shuffles.
 template <bool CODES>
 __global__ __launch_bounds__(kRequantThreads) void mxfp8_requant_kernel(const float* __restrict__ inter32,
                                                                         uint16_t* __restrict__ inter,
@@ -76,15 +54,7 @@ __global__ __launch_bounds__(kRequantThreads) void mxfp8_requant_kernel(const fl
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
       amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-      // ceil(log2(amax / 448)) exactly: amax = fr 2^ex with fr in [0.5, 1); amax / 448 =
-      // (fr / 0.875) 2^(ex - 9), and fr / 0.875 lies in [0.57, 1.15): above 1 only for fr > 0.875.
-      int e = 0;
-      if (amax > 0.f) {
-        const int ex = __builtin_amdgcn_frexp_expf(amax);
-        const float fr = __builtin_amdgcn_frexp_mantf(amax);
-        e = ex - 9 + (fr > 0.875f ? 1 : 0);
-        e = e < -127 ? -127 : (e > 127 ? 127 : e);
-      }
+      const int e = amax > 0.f ? mx8_exponent(amax) : 0;
       if constexpr (CODES) {
         uint32_t w[2] = {0u, 0u};
 #pragma unroll
