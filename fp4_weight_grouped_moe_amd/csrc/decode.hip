@@ -577,14 +577,13 @@ __host__ __device__ inline size_t f3_lds_bytes(int64_t m, int64_t topk, int64_t 
 }
 
 // W8 (W4A8, block-scaled MFMA): each route's K slice as MXFP8 codes (256 B) and its 8 E8M0
-// bytes, plus a 1 KiB fragment-transposition area per wave.
+// bytes.
 constexpr int kF8RowBytes = kF3KB * kKBlock;
 __host__ __device__ inline size_t f8_rows_bytes(int64_t routes) { return (size_t(routes) * kF8RowBytes + 1023) / 1024 * 1024; }
 __host__ __device__ inline size_t f8_scale_bytes(int64_t routes) { return (size_t(routes) * 8 + 15) / 16 * 16; }
-constexpr size_t kF8Transpose = size_t(kF3Waves) * 1024;
 template <int RG>
 __host__ __device__ inline size_t f8_lds_bytes(int64_t m, int64_t topk, int64_t cap_blocks) {
-  return f8_rows_bytes(m * topk) + f8_scale_bytes(m * topk) + kF8Transpose + f3_table_bytes(cap_blocks) +
+  return f8_rows_bytes(m * topk) + f8_scale_bytes(m * topk) + f3_table_bytes(cap_blocks) +
          f3_exp_bytes(m * topk) + size_t(kF3Waves) * m * 16 * RG * 4;
 }
 
@@ -609,10 +608,9 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
   if (G >= ngroup || z >= nsplit) return;
   const int kq0 = z * kF3KB;
   uint8_t* bs = dyn;                                                        // [routes][kF3RowBytes] (W8: kF8RowBytes)
-  // W8: E8M0 bytes [routes][8] and the per-wave transposition areas after the rows
+  // W8: E8M0 bytes [routes][8] after the code rows
   uint32_t* ssc = reinterpret_cast<uint32_t*>(dyn + f8_rows_bytes(routes));
-  uint32_t* xtr = reinterpret_cast<uint32_t*>(dyn + f8_rows_bytes(routes) + f8_scale_bytes(routes)) + wave * 256;
-  int* sroute = reinterpret_cast<int*>(dyn + (W8 ? f8_rows_bytes(routes) + f8_scale_bytes(routes) + kF8Transpose
+  int* sroute = reinterpret_cast<int*>(dyn + (W8 ? f8_rows_bytes(routes) + f8_scale_bytes(routes)
                                                   : f3_rows_bytes(routes)));   // [nb * 16] slot -> route
   int* sexp = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(sroute) + f3_table_bytes(p.cap_blocks));    // [routes] f16 exponents
   float* tacc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sexp) + f3_exp_bytes(routes));          // [waves][m][16 RG]
@@ -627,30 +625,57 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
     for (int r = tid; r < routes; r += kF3Threads) sexp[r] = __float_as_int(p.topk_weights[r]);
   const __amdgpu_buffer_rsrc_t tr = buffer_rsrc(p.sorted_route_ids, uint32_t(nb * kBlockM * 4));
   for (int n = wave; n * 64 < nb * kBlockM; n += kF3Waves) dma4(tr, sroute + 64 * n, uint32_t((64 * n + lane) * 4));
-  // The route -> slot lookups of all of a wave's rows go out together, then the row DMAs.
-  constexpr int kRowB = W8 ? kF8RowBytes : kF3RowBytes;     // staged bytes per route
-  constexpr int kElB = W8 ? 1 : 2;                           // bytes per element
-  const __amdgpu_buffer_rsrc_t ir = W8 ? buffer_rsrc(p.inter8, uint32_t(p.cap_blocks * kBlockM * g.ip))
-                                       : buffer_rsrc(p.inter, uint32_t(p.cap_blocks * kBlockM * g.ip * 2));
-  const int nchunk = int((W8 ? f8_rows_bytes(routes) : f3_rows_bytes(routes)) / 1024);
-  int slot[kF3MaxRowDma];
+  // W8: this split's K slice of every route rounded to MXFP8 here, from FC1's fp32 rows: task
+  // t covers 8 values, quarter t % 4 of MX group (t / 4) % 8 of route t / 32, so the four tasks
+  // of a group sit in adjacent lanes. Dropped routes and K blocks past kb2 give zero codes.
+  // The first tasks' loads go out ahead of the weight loads below.
+  constexpr int kPre = 2;                                    // tasks per thread loaded ahead
+  const int ntask = routes * 32;
+  f32x4 pre[kPre][2];
+  auto load_task = [&](int t, f32x4* v) {
+    v[0] = v[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t < ntask) {
+      const int r = t >> 5, kblk = kq0 + ((t >> 4) & 1);
+      const int sl = p.route_slot[r];
+      if (sl >= 0 && kblk < kb2) {
+        const float* src = p.inter32 + int64_t(sl) * g.ip + int64_t(kq0) * kKBlock + (t & 31) * 8;
+        v[0] = *reinterpret_cast<const f32x4*>(src);
+        v[1] = *reinterpret_cast<const f32x4*>(src + 4);
+      }
+    }
+  };
+  auto round_task = [&](int t, const f32x4* v) {
+    float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < kF3MaxRowDma; ++i) {
-    const int n = wave + kF3Waves * i, r = (n * 1024 + lane * 16) / kRowB;
-    slot[i] = n < nchunk && r < routes ? p.route_slot[r] : -1;
-  }
-#pragma unroll
-  for (int i = 0; i < kF3MaxRowDma; ++i) {
-    const int n = wave + kF3Waves * i, o = (n * 1024 + lane * 16) % kRowB;
-    const bool ok = slot[i] >= 0 && kq0 + o / (kKBlock * kElB) < kb2;
-    if (n < nchunk) dma16(ir, bs + n * 1024, ok ? uint32_t((slot[i] * g.ip + kq0 * kKBlock) * kElB + o) : kOutOfRange);
-  }
+    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(v[0][i]), fabsf(v[1][i])));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int e = amax > 0.f ? mx8_exponent(amax) : 0;
+    const float lo[4] = {v[0][0], v[0][1], v[0][2], v[0][3]}, hi[4] = {v[1][0], v[1][1], v[1][2], v[1][3]};
+    if (t < ntask) {
+      *reinterpret_cast<uint2*>(bs + (t >> 5) * kF8RowBytes + (t & 31) * 8) =
+          make_uint2(mx8_codes4(lo, e, amax), mx8_codes4(hi, e, amax));
+      if ((t & 3) == 0) reinterpret_cast<uint8_t*>(ssc)[(t >> 5) * 8 + ((t >> 2) & 7)] = uint8_t(amax > 0.f ? e + 127 : 0);
+    }
+  };
   if constexpr (W8) {
-    // each route's two scale dwords (K blocks kq0, kq0 + 1; 2^0 where there is no route or block)
-    for (int i = tid; i < 2 * routes; i += kF3Threads) {
-      const int r = i >> 1, h = i & 1, sl = p.route_slot[r];
-      ssc[i] = sl >= 0 && kq0 + h < kb2 ? *reinterpret_cast<const uint32_t*>(p.sc8 + int64_t(sl) * (g.ip / 32) + (kq0 + h) * 4)
-                                        : 0x7F7F7F7Fu;
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) load_task(i * kF3Threads + tid, pre[i]);
+  } else {
+    // The route -> slot lookups of all of a wave's rows go out together, then the row DMAs.
+    const __amdgpu_buffer_rsrc_t ir = buffer_rsrc(p.inter, uint32_t(p.cap_blocks * kBlockM * g.ip * 2));
+    const int nchunk = int(f3_rows_bytes(routes) / 1024);
+    int slot[kF3MaxRowDma];
+#pragma unroll
+    for (int i = 0; i < kF3MaxRowDma; ++i) {
+      const int n = wave + kF3Waves * i, r = (n * 1024 + lane * 16) / kF3RowBytes;
+      slot[i] = n < nchunk && r < routes ? p.route_slot[r] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < kF3MaxRowDma; ++i) {
+      const int n = wave + kF3Waves * i, o = (n * 1024 + lane * 16) % kF3RowBytes;
+      const bool ok = slot[i] >= 0 && kq0 + o / (kKBlock * 2) < kb2;
+      if (n < nchunk) dma16(ir, bs + n * 1024, ok ? uint32_t((slot[i] * g.ip + kq0 * kKBlock) * 2 + o) : kOutOfRange);
     }
   }
 
@@ -685,6 +710,15 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
   if (U > 0) {
     issue(0, ra);
     issue(1, rb);
+  }
+  if constexpr (W8) {
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) round_task(i * kF3Threads + tid, pre[i]);
+    for (int t0 = kPre * kF3Threads; t0 < ntask; t0 += kF3Threads) {
+      f32x4 v[2];
+      load_task(t0 + tid, v);
+      round_task(t0 + tid, v);
+    }
   }
   wait_vmcnt<0>();
   lds_barrier();
@@ -721,7 +755,7 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
     if (u >= U) return;
     const int blk = wave + u * kF3Waves;
     const int route = sroute[blk * kBlockM + col];
-    const uint8_t* brow = bs + max(route, 0) * kRowB + q * 16;
+    const uint8_t* brow = bs + max(route, 0) * (W8 ? kF8RowBytes : kF3RowBytes) + q * 16;
     f32x4 acc[RG];
 #pragma unroll
     for (int rr = 0; rr < RG; ++rr) acc[rr] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -730,8 +764,8 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
       // lane (col, q) holds K 16 q .. 16 q + 15 and 64 + 16 q .. 64 + 16 q + 15 of route col; its
       // scale byte is block q of that route. A (the weights): lane (col, q) must hold the 32
       // consecutive K of block q of row col, while the fragment layout deals them out in
-      // 8-K chunks over the four lane quarters (chunk 4 s + q in dword s): a 4 x 4 transpose
-      // through this wave's LDS area (LDS operations of one wave complete in order).
+      // 8-K chunks over the four lane quarters (chunk 4 s + q in dword s): a 4 x 4 dword
+      // transpose across the quarters (gfx950 lane swaps).
 #pragma unroll
       for (int j = 0; j < kF3KB; ++j) {
         if (kq0 + j < kb2) {
@@ -741,9 +775,7 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
           const int sb = route >= 0 ? int((ssc[route * 2 + j] >> (8 * q)) & 0xFFu) : 127;
 #pragma unroll
           for (int rr = 0; rr < RG; ++rr) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) xtr[col * 16 + 4 * s + q] = r.q[rr][j][s];
-            const u32x4 a = *reinterpret_cast<const u32x4*>(xtr + col * 16 + 4 * q);
+            const u32x4 a = transpose_quarters(r.q[rr][j]);
             const i32x8 aop = i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]), 0, 0, 0, 0};
             const int sa = int((r.s[rr][j] >> (8 * q)) & 0xFFu);
             acc[rr] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, acc[rr], 4, 0, 0, sa, 0, sb);
@@ -876,8 +908,9 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
   // FC2 multiplies their exact values in bf16
   const bool w8 = FMT == FMT_MXFP4 && p.w4a8 && p.inter8 != nullptr && split &&
                   f8_lds_bytes<RG>(p.m, p.topk, p.cap_blocks) <= size_t(kF3MaxLds);
-  if (p.w4a8) {
-    if (hipError_t e = launch_mxfp8_requant(p, w8, stream); e != hipSuccess) return e;
+  if (p.w4a8 && !w8) {
+    // (the block-scaled FC2 rounds its own slices; the bf16 fallback needs the rounding pass)
+    if (hipError_t e = launch_mxfp8_requant(p, false, stream); e != hipSuccess) return e;
     if (marks) marks->after(stream, KID_REQUANT);
   }
   if (split) {
