@@ -364,7 +364,7 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   fp.inter = reinterpret_cast<uint16_t*>(ws + fg.off_inter);
   fp.x16 = rp.x16;
   fp.xexp = rp.xexp;
-  fp.y = reinterpret_cast<float*>(ws + fg.off_y);
+  fp.y = reinterpret_cast<uint16_t*>(ws + fg.off_y);
   fp.part = reinterpret_cast<float*>(ws + fg.off_part);
   fp.f2_count = decode ? reinterpret_cast<int32_t*>(ws + fg.off_count) : nullptr;
   fp.cap_blocks = pg.cap_blocks;

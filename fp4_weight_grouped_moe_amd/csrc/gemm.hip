@@ -16,7 +16,7 @@
 //  * FC1 epilogue: expert FC1 global scale, SiLU-SwiGLU (gate and up fragments sit in the
 //    same lanes) or relu2, times router weight and the expert's FC2 global scale, bf16 store
 //    into the intermediate row of the route's slot.
-//  * FC2 epilogue: the weighted row of each route in fp32; the combine pass sums each
+//  * FC2 epilogue: the weighted row of each route rounded to bf16; the combine pass sums each
 //    token's top-k rows in a fixed order (deterministic, no atomics) and casts to bf16.
 // NVFP4 FC1 runs on f16 operands: activations pre-scaled per token by a power of two, E2M1 x
 // E4M3 products exact in f16 (half the dequantisation work of the bf16 route).
@@ -62,6 +62,12 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maxima
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Four consecutive columns of a route's weighted FC2 row, rounded to bf16 (the combine pass sums
+// a token's rows in fp32).
+__device__ __forceinline__ void store_row4(uint16_t* dst, const f32x4& v) {
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
 // Per-launch constants shared by every item of a workgroup.
@@ -412,7 +418,7 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
 #pragma unroll
           for (int f = 0; f < FR; ++f) {
             const int64_t h = int64_t(rg_base + f) * 16 + r0;
-            if (h < g.H) *reinterpret_cast<f32x4*>(p.y + int64_t(r) * g.H + h) = acc[f][bb] * wt;
+            if (h < g.H) store_row4(p.y + int64_t(r) * g.H + h, acc[f][bb] * wt);
           }
         }
       }
@@ -575,7 +581,7 @@ __device__ __forceinline__ void gemm_item_w8(const FusedParams& p, const GemmCtx
     if (kb + j < kbs) step(kb + j, j);
   wait_vmcnt<0>();
 
-  // Epilogue: the weighted fp32 row of each route (router weight x FC2 global scale, outside
+  // Epilogue: the weighted bf16 row of each route (router weight x FC2 global scale, outside
   // the quantisation), summed over top-k by the combine pass.
   const int r0 = 4 * q;
 #pragma unroll
@@ -587,7 +593,7 @@ __device__ __forceinline__ void gemm_item_w8(const FusedParams& p, const GemmCtx
 #pragma unroll
         for (int f = 0; f < FR; ++f) {
           const int64_t hh = int64_t(rg_base + f) * 16 + r0;
-          if (hh < g.H) *reinterpret_cast<f32x4*>(p.y + int64_t(r) * g.H + hh) = acc[f][b] * wt;
+          if (hh < g.H) store_row4(p.y + int64_t(r) * g.H + hh, acc[f][b] * wt);
         }
       }
     }
@@ -686,18 +692,35 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
   }
 }
 
-// out[t] = bf16(sum over the token's valid routes of y[route]) in route order j = 0..k-1.
-__global__ void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ route_slot,
+// out[t] = bf16(sum over the token's valid routes of y[route]) in route order j = 0..k-1, the
+// sum in fp32 over the routes' bf16 rows. A thread owns 8 columns of a token; the rows of up
+// to 8 routes are loaded together, then added in order.
+__global__ void combine_kernel(const uint16_t* __restrict__ y, const int32_t* __restrict__ route_slot,
                                uint16_t* __restrict__ out, int64_t m, int topk, int64_t H) {
-  const int64_t q = H / 4;
+  const int64_t q = H / 8;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < m * q; i += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t t = i / q, c4 = (i % q) * 4;
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < topk; ++j) {
-      const int64_t r = t * topk + j;
-      if (route_slot[r] >= 0) s += *reinterpret_cast<const f32x4*>(y + r * H + c4);
+    const int64_t t = i / q, c8 = (i % q) * 8;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < topk; j0 += 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t r = t * topk + j0 + u;
+        v[u] = j0 + u < topk && route_slot[r] >= 0 ? *reinterpret_cast<const u32x4*>(y + r * H + c8) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (j0 + u < topk) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            s[2 * w] += __uint_as_float(v[u][w] << 16);
+            s[2 * w + 1] += __uint_as_float(v[u][w] & 0xFFFF0000u);
+          }
+        }
+      }
     }
-    *reinterpret_cast<uint2*>(out + t * H + c4) = make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
+    *reinterpret_cast<u32x4*>(out + t * H + c8) =
+        u32x4{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]), pack_bf16x2(s[4], s[5]), pack_bf16x2(s[6], s[7])};
   }
 }
 
@@ -739,7 +762,7 @@ hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, La
 }
 
 void launch_combine(const FusedParams& p, hipStream_t stream) {
-  const int64_t n = p.m * p.g.H / 4;
+  const int64_t n = p.m * p.g.H / 8;
   int64_t cb = (n + 255) / 256;
   if (cb < 1) cb = 1;
   if (cb > 8192) cb = 8192;

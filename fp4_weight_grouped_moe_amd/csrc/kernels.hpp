@@ -79,7 +79,7 @@ struct FusedParams {
   // and FC2 on the block-scaled MFMA, applying router weight x FC2 global scale per route.
   int32_t w4a8;
   // Grouped-GEMM path, opt-in: FC2 adds each route's weighted row into the bf16 output with
-  // packed-bf16 atomics (FC1 zeroes the output first); no fp32 rows, no combine pass.
+  // packed-bf16 atomics (FC1 zeroes the output first); no per-route rows, no combine pass.
   int32_t atomic_bf16;
   float* inter32;                // W4A8, decode path: fp32 [cap_routes, ip] activation output of FC1
   uint8_t* inter8;               // W4A8: MXFP8 codes [cap_routes, ip] (E4M3)
@@ -87,7 +87,7 @@ struct FusedParams {
   uint16_t* inter;               // bf16 [cap_routes, ip]
   const uint16_t* x16;           // f16 [m, H] scaled activations (NVFP4 f16 MFMA route)
   const int32_t* xexp;           // [m] their per-token exponents
-  float* y;                      // fp32 [m * topk, H] weighted FC2 rows per route (grouped GEMM)
+  uint16_t* y;                   // bf16 [m * topk, H] weighted FC2 rows per route (grouped GEMM)
   float* part;                   // fp32 [K splits, m, H] FC2 partial sums (decode)
   int32_t* f2_count;             // [n2_groups] FC2 K-split arrival counts (decode)
   int64_t cap_blocks;

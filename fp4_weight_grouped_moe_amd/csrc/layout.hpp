@@ -108,7 +108,7 @@ inline bool decode_stages_x(const PreparedGeom& g, int64_t m) { return m * decod
 
 // Fused-layer workspace: route pack (block 16), bf16 intermediate rows per packed slot, the
 // f16 copy of the activations with per-token exponents (NVFP4), for the grouped-GEMM path
-// the fp32 FC2 row of every route, summed over top-k by the combine pass, and for the
+// the bf16 FC2 row of every route, summed over top-k by the combine pass, and for the
 // decode path the fp32 FC2 partial sums of each K split with their arrival counts.
 struct FusedGeom {
   PackGeom pack;
@@ -131,7 +131,7 @@ __host__ __device__ inline FusedGeom make_fused_geom(const PreparedGeom& w, int6
   f.off_sc8 = o;    o = align256(o + (w8 ? size_t(f.pack.cap_routes) * (w.ip / 32) : 0));
   f.off_x16 = o;   o = align256(o + size_t(cap) * w.H * 2);
   f.off_xexp = o;  o = align256(o + size_t(cap) * 4);
-  f.off_y = o;     o = align256(o + size_t(cap) * k * w.H * 4);
+  f.off_y = o;     o = align256(o + size_t(cap) * k * w.H * 2);
   // decode FC2 partial sums: one fp32 [cap, H] slab per pair of intermediate K blocks
   f.off_part = o;  o = align256(o + (cap <= kDecodeMaxM ? size_t((w.kb2 + 1) / 2) * cap * w.H * 4 : 0));
   f.off_count = o; o = align256(o + (cap <= kDecodeMaxM ? size_t(w.n2_groups) * 4 : 0));

@@ -170,9 +170,9 @@ int moe_w4a16_prepare_layout(const moe_w4a16_dims* dims, const moe_w4a16_source_
  * each workgroup a range of hidden rows and a slice of K for every route, sums each
  * token's routes in LDS, and the last K slice of a row range to finish adds the slices in
  * order before one bf16 store. Other calls take the grouped-GEMM path: FC1 + activation
- * epilogue over (route tile, weight tile) items, FC2 writing each route's weighted fp32
- * row, and a combine pass that sums every token's top-k rows in route order and casts to
- * bf16 -- deterministic, no atomics on data. Persistent workgroups take items from a
+ * epilogue over (route tile, weight tile) items, FC2 writing each route's weighted row
+ * rounded to bf16, and a combine pass that sums every token's top-k rows in fp32 in route
+ * order and casts to bf16 -- deterministic, no atomics on data. Persistent workgroups take items from a
  * queue; no workgroup waits on another that may not be resident. */
 #define MOE_DECODE_MAX_M 16
 
@@ -218,10 +218,11 @@ int moe_w4a16_fused_device_m(const moe_w4a16_dims* dims, const void* prepared, s
  * out[t] = sum_j w[t, j] * W2_e @ MXFP8(act(W13_e @ x_t)) over surviving routes.
  * Arguments, layouts, ownership and errors as moe_w4a16_fused (same prepared buffer and
  * workspace); MOE_ERR_UNSUPPORTED unless dims->fmt is MOE_FMT_MXFP4_E8M0_K32 (the gfx950
- * block-scaled MFMA applies E8M0 scales only). FC1 keeps the activation output in fp32 for
- * the rounding (one rounding, as defined); the decode path's FC2 multiplies the E4M3 codes on
- * gfx950's block-scaled FP4 x FP8 MFMA, the grouped-GEMM path's the exact MXFP8 values on the
- * bf16 MFMA. */
+ * block-scaled MFMA applies E8M0 scales only). The rounding is taken from FC1's fp32 result
+ * (one rounding, as defined): in the grouped-GEMM path's FC1 epilogue, on the decode path by
+ * each FC2 workgroup for its K slice. FC2 multiplies the E4M3 codes on gfx950's block-scaled
+ * FP4 x FP8 MFMA on both paths (the decode path falls back to the exact MXFP8 values on the
+ * bf16 MFMA when the routes' slices do not fit in its LDS). */
 int moe_w4a8_fused(const moe_w4a16_dims* dims, const void* prepared, size_t prepared_bytes,
                    const uint16_t* x, int64_t m, const int32_t* topk_ids,
                    const float* topk_weights, int topk, const int32_t* expert_map,
@@ -233,8 +234,8 @@ int moe_w4a8_fused(const moe_w4a16_dims* dims, const void* prepared, size_t prep
  * atomically, offered as an opt-in approximate mode beside the f32 reduction). The same layer
  * as moe_w4a16_fused; on the grouped-GEMM path (m above the decode threshold) FC2 rounds each
  * route's weighted row to bf16 and adds it into its token's output row with gfx950's
- * packed-bf16 global atomic (FC1 zeroes `out` first), instead of writing fp32 rows for the
- * fixed-order combine pass. Every partial sum is rounded to bf16 and the order of the adds
+ * packed-bf16 global atomic (FC1 zeroes `out` first), instead of writing per-route rows for
+ * the fixed-order combine pass. Every partial sum is rounded to bf16 and the order of the adds
  * varies, so results can differ from run to run and from moe_w4a16_fused by a few bf16 ulps
  * of the row's magnitude. On the decode path it is moe_w4a16_fused exactly (that path sums
  * the top-k in registers). Arguments, layouts, ownership and errors as moe_w4a16_fused. */
