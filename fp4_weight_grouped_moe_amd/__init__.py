@@ -46,7 +46,7 @@ class moe_w4a16_dims(ctypes.Structure):
 
 class moe_w4a16_source_layout(ctypes.Structure):
     _fields_ = [("w13_up_first", ctypes.c_int32), ("global_scale_reciprocal", ctypes.c_int32),
-                ("scale_per_row", ctypes.c_int32)]
+                ("scale_per_row", ctypes.c_int32), ("w13_interleaved", ctypes.c_int32)]
 
 
 class moe_route_pack_view(ctypes.Structure):

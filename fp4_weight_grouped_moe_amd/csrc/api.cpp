@@ -229,7 +229,8 @@ int moe_w4a16_prepare_layout(const moe_w4a16_dims* dims, const moe_w4a16_source_
   if (int rc = check_dims(dims)) return rc;
   moe_w4a16_source_layout lay{};
   if (layout) lay = *layout;
-  if ((lay.w13_up_first & ~1) || (lay.global_scale_reciprocal & ~1) || (lay.scale_per_row & ~1))
+  if ((lay.w13_up_first & ~1) || (lay.global_scale_reciprocal & ~1) || (lay.scale_per_row & ~1) ||
+      (lay.w13_interleaved & ~1))
     return fail(MOE_ERR_INVALID_ARG, "source layout flags must be 0 or 1");
   if (!w13 || !s13 || !w2 || !s2) return fail(MOE_ERR_INVALID_ARG, "a weight or scale pointer is NULL");
   if (dims->fmt == MOE_FMT_NVFP4_E4M3_K16 && (!g13 || !g2))
@@ -245,6 +246,7 @@ int moe_w4a16_prepare_layout(const moe_w4a16_dims* dims, const moe_w4a16_source_
   pp.w2 = w2; pp.s2 = s2; pp.g2 = g2;
   pp.out = static_cast<uint8_t*>(prepared);
   pp.w13_up_first = lay.w13_up_first;
+  pp.w13_interleaved = lay.w13_interleaved;
   pp.global_reciprocal = lay.global_scale_reciprocal;
   pp.scale_per_row = lay.scale_per_row;
   return launch_status(launch_prepare(pp, stream), "prepare launch");

@@ -44,6 +44,7 @@ struct PrepareParams {
   uint8_t* out;
   // Source layout variants (all 0: canonical).
   int32_t w13_up_first;          // SwiGLU W13 rows [0, I) are up, [I, 2I) gate
+  int32_t w13_interleaved;       // SwiGLU W13 rows alternate between the halves
   int32_t global_reciprocal;     // g13 / g2 hold 1 / (dequant multiplier)
   int32_t scale_per_row;         // one scale byte per row for all of K: s [E, N, 1]
 };

@@ -22,10 +22,14 @@ __device__ __forceinline__ int64_t fc1_row(const PreparedGeom& g, int64_t rg, in
   return i < g.I ? i : -1;
 }
 
-// Source row of canonical FC1 row `row` (up-half-first checkpoints swap the halves).
+// Source row of canonical FC1 row `row`: up-half-first checkpoints swap the halves,
+// row-interleaved ones store row i of the first half at 2i and of the second at 2i + 1.
 __device__ __forceinline__ int64_t fc1_src_row(const PrepareParams& p, int64_t row) {
-  if (row < 0 || !p.w13_up_first || p.g.act != ACT_SWIGLU) return row;
-  return row < p.g.I ? row + p.g.I : row - p.g.I;
+  if (row < 0 || p.g.act != ACT_SWIGLU) return row;
+  int64_t half = row < p.g.I ? 0 : 1;
+  const int64_t i = row - half * p.g.I;
+  half ^= p.w13_up_first;
+  return p.w13_interleaved ? 2 * i + half : half * p.g.I + i;
 }
 
 __device__ __forceinline__ int64_t fc2_row(const PreparedGeom& g, int64_t rg, int r) {

@@ -145,6 +145,10 @@ int moe_w4a16_prepare(const moe_w4a16_dims* dims, const uint8_t* w13, const uint
  *                            MXFP4.
  *   scale_per_row            s13 is [E, N1, 1] and s2 [E, H, 1]: one scale byte per row for
  *                            all of K (group size -1).
+ *   w13_interleaved          SwiGLU W13 rows (and s13 rows) alternate between the halves:
+ *                            row 2i is row i of the first half, 2i + 1 row i of the second
+ *                            (the first half is gate, or up with w13_up_first); ignored for
+ *                            relu2.
  * The prepared buffer equals, byte for byte, the one moe_w4a16_prepare makes from the
  * canonical arrays these describe. layout may be NULL (canonical). Errors as for
  * moe_w4a16_prepare, plus MOE_ERR_INVALID_ARG for a flag outside {0, 1}. */
@@ -152,6 +156,7 @@ typedef struct moe_w4a16_source_layout {
   int32_t w13_up_first;
   int32_t global_scale_reciprocal;
   int32_t scale_per_row;
+  int32_t w13_interleaved;
 } moe_w4a16_source_layout;
 
 int moe_w4a16_prepare_layout(const moe_w4a16_dims* dims, const moe_w4a16_source_layout* layout,

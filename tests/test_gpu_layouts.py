@@ -34,7 +34,12 @@ def moe():
     return m
 
 
-def _variant(cfg, seed, up_first, reciprocal, per_row):
+def _interleave(a, inter):
+    """The two W13 halves stored row by row alternately (rows 2i, 2i + 1 = row i of each)."""
+    return np.stack([a[:, :inter], a[:, inter:]], axis=2).reshape(a.shape)
+
+
+def _variant(cfg, seed, up_first, reciprocal, per_row, interleaved=0):
     """A source-layout variant drawn at random: (w13, s13, g13, w2, s2, g2) as stored."""
     codes = D.draw_random_codes(cfg, seed)
     w13, s13, g13, w2, s2, g2 = (codes[k] for k in ("w13", "s13", "g13", "w2", "s2", "g2"))
@@ -44,6 +49,9 @@ def _variant(cfg, seed, up_first, reciprocal, per_row):
     if up_first and cfg.act == "silu_swiglu":
         w13 = L.w13_gate_first(w13, cfg.inter)          # the swap is its own inverse
         s13 = L.w13_gate_first(s13, cfg.inter)
+    if interleaved and cfg.act == "silu_swiglu":
+        w13 = _interleave(w13, cfg.inter)
+        s13 = _interleave(s13, cfg.inter)
     if reciprocal and cfg.fmt == "nvfp4":
         g13 = (np.float32(1) / np.asarray(g13, np.float32)).astype(np.float32)
         g2 = (np.float32(1) / np.asarray(g2, np.float32)).astype(np.float32)
@@ -92,6 +100,8 @@ def test_prepare_layout_rejects_bad_flags(moe, device):
     buf = torch.empty(size, dtype=torch.uint8, device=device)
     with pytest.raises(moe.MoeError):
         moe.moe_w4a16_prepare_layout(dims, moe.moe_w4a16_source_layout(2, 0, 0), buf, buf, buf, buf, buf, buf, buf, size)
+    with pytest.raises(moe.MoeError):
+        moe.moe_w4a16_prepare_layout(dims, moe.moe_w4a16_source_layout(0, 0, 0, 3), buf, buf, buf, buf, buf, buf, buf, size)
 
 
 def _odd(base, H, I):
@@ -115,6 +125,22 @@ def test_prepare_layout_equals_canonical_odd_shapes(moe, device, cfg, up_first, 
     canon = L.canonical(cfg.fmt, cfg.act, cfg.hidden, cfg.inter, *var, w13_up_first=bool(up_first),
                         global_scale_reciprocal=bool(reciprocal), scale_per_row=bool(per_row))
     layout = moe.moe_w4a16_source_layout(up_first, reciprocal, per_row)
+    got = _prepare(moe, device, cfg, var, layout)
+    want = _prepare(moe, device, cfg, canon, None)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} prepared bytes differ, first at {bad[:8]}"
+
+
+@pytest.mark.parametrize("cfg", [SCALED["decode_s"], SCALED["edge_s"], SCALED["small_s"]] + ODD, ids=lambda c: c.name)
+@pytest.mark.parametrize("up_first,per_row", [(0, 0), (1, 0), (1, 1)])
+def test_prepare_layout_row_interleaved_w13(moe, device, cfg, up_first, per_row):
+    """W13 (and its scales) stored with the gate and up rows alternating, alone and with the
+    up half first: prepared byte for byte as the canonical arrays (relu2 ignores the flag)."""
+    print(f"layout {cfg.name} interleaved up_first={up_first} per_row={per_row}", flush=True)
+    var = _variant(cfg, 131 + 8 * up_first + 2 * per_row, up_first, 0, per_row, interleaved=1)
+    canon = L.canonical(cfg.fmt, cfg.act, cfg.hidden, cfg.inter, *var, w13_up_first=bool(up_first),
+                        scale_per_row=bool(per_row), w13_interleaved=True)
+    layout = moe.moe_w4a16_source_layout(up_first, 0, per_row, 1)
     got = _prepare(moe, device, cfg, var, layout)
     want = _prepare(moe, device, cfg, canon, None)
     bad = np.flatnonzero(got != want)

@@ -15,6 +15,19 @@ def test_half_swap_hand_case():
     np.testing.assert_array_equal(L.w13_gate_first(got, 2), rows)     # swapping twice is the identity
 
 
+def test_interleave_hand_case():
+    # I = 2, rows stored alternately: g0 u0 g1 u1 (gate first) -> g0 g1 u0 u1
+    rows = np.array([[[10], [20], [11], [21]]], np.uint8)
+    assert L.w13_halves(rows, 2)[0, :, 0].tolist() == [10, 11, 20, 21]
+    with pytest.raises(ValueError):
+        L.w13_halves(np.zeros((1, 3, 1), np.uint8), 2)
+    # with the up half first: u0 g0 u1 g1 -> canonical g0 g1 u0 u1
+    up_first = np.array([[[20, 20], [10, 10], [21, 21], [11, 11]]], np.uint8)
+    c = L.canonical("mxfp4", "silu_swiglu", 64, 2, up_first, up_first, None, None, None, None,
+                    w13_up_first=True, w13_interleaved=True)
+    assert c[0][0, :, 0].tolist() == [10, 11, 20, 21] and c[1][0, :, 1].tolist() == [10, 11, 20, 21]
+
+
 def test_half_swap_rejects_wrong_rows():
     with pytest.raises(ValueError):
         L.w13_gate_first(np.zeros((1, 3, 2), np.uint8), 2)
@@ -53,11 +66,13 @@ def test_dequantised_weights_do_not_depend_on_layout(fmt):
     r2 = rng.integers(*band, size=(e, h, 1), dtype=np.uint8)
     g13 = np.array([2.0, 0.5], np.float32)
     g2 = np.array([0.25, 4.0], np.float32)
-    # the variant: up half first, encode-sense globals, per-row scales
-    v13 = np.concatenate([w13[:, i:], w13[:, :i]], axis=1)
-    vr13 = np.concatenate([r13[:, i:], r13[:, :i]], axis=1)
+    # the variant: up half first, rows interleaved, encode-sense globals, per-row scales
+    def stored(a):
+        a = np.concatenate([a[:, i:], a[:, :i]], axis=1)                # up half first
+        return np.stack([a[:, :i], a[:, i:]], axis=2).reshape(a.shape)  # then row by row
+    v13, vr13 = stored(w13), stored(r13)
     c = L.canonical(fmt, "silu_swiglu", h, i, v13, vr13, np.float32(1) / g13, w2, r2, np.float32(1) / g2,
-                    w13_up_first=True, global_scale_reciprocal=True, scale_per_row=True)
+                    w13_up_first=True, global_scale_reciprocal=True, scale_per_row=True, w13_interleaved=True)
     want13 = F.dequant(fmt, w13, np.repeat(r13, h // group, axis=2), g13 if fmt == "nvfp4" else None)
     got13 = F.dequant(fmt, c[0], c[1], c[2] if fmt == "nvfp4" else None)
     np.testing.assert_array_equal(got13, want13)
