@@ -158,6 +158,11 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const uint8_t* l
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, int(voff), 0, 0, 0);
 }
 
+// The same with a wave-uniform part of the offset in the scalar offset (no VALU add per load).
+__device__ __forceinline__ void dma16s(__amdgpu_buffer_rsrc_t r, const uint8_t* lds_dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, int(voff), int(soff), 0, 0);
+}
+
 // 4 bytes per lane from a buffer into LDS at lds_dst + 4 * lane.
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const void* lds_dst, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 4, int(voff), 0, 0, 0);

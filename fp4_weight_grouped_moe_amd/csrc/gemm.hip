@@ -111,7 +111,9 @@ __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, const f32
 __device__ __forceinline__ f32x4 mma(const f16x8& a, const f16x8& b, const f32x4& c) { return mfma16h(a, b, c); }
 
 // One item: NB route blocks (16 NB rows) of one expert x 256 weight rows, full K.
-template <int FMT, int PHASE, int NB>
+// KT: the activation K extent is not a multiple of the 256-byte K block (hidden size not a
+// multiple of 128): every activation load checks its lane's offset against the row end.
+template <int FMT, int PHASE, int NB, bool KT>
 __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c, uint8_t* lds, int mt, int nt) {
   using P = Plan<NB>;
   constexpr int D = P::kDepth, FR = P::FR, BW = P::BW, XD = P::XD;
@@ -161,6 +163,14 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
       __builtin_amdgcn_readfirstlane(int(tile_groups * c.sc_per_group)), 0x00020000);
   const int rg_base = nt * 16 + wave * FR;
   const int sc_lane = FMT == FMT_NVFP4 ? ((lane >> 5) * 16 + (lane & 15)) * 16 : (lane & 15) * 16;
+  // the lane's constant parts of the weight and scale offsets (the K block's part goes in the
+  // scalar offset of each load)
+  int wvoff[FR], svoff[FR];
+#pragma unroll
+  for (int f = 0; f < FR; ++f) {
+    wvoff[f] = (wave * FR + f) * kbs * kFragBytes + lane * 16;
+    svoff[f] = int((wave * FR + f) * c.sc_per_group) + sc_lane;
+  }
 
   // One stage: the activation K block into LDS slot `slot`, this wave's fragment dwords and
   // scale dwords into registers. Blocks past K are clamped (weights) or read 0 (activations):
@@ -179,15 +189,16 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
     for (int l = 0; l < P::kLoads; ++l) {
       if (l * 4 / P::kLoads != part) continue;
       if (l < FR) {
-        scd[l] = __builtin_amdgcn_raw_buffer_load_b32(
-            sres, int((wave * FR + l) * c.sc_per_group + (kc >> 2) * g.sc_chunk_bytes) + sc_lane + (kc & 3) * 4, 0, 0);
+        scd[l] = __builtin_amdgcn_raw_buffer_load_b32(sres, svoff[l], int((kc >> 2) * g.sc_chunk_bytes + (kc & 3) * 4), 0);
       } else if (l < 2 * FR) {
         const int f = l - FR;
-        wd[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-            wres, ((wave * FR + f) * kbs + kc) * kFragBytes + lane * 16, 0, 0));
+        wd[f] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, wvoff[f], kc * kFragBytes, 0));
       } else {
         const int j = l - 2 * FR;
-        dma16(c.act, st + qdst[j], (rowoff[j] + k + gofs[j]) | (k + gofs[j] < uint32_t(c.k_bytes) ? 0u : kOutOfRange));
+        if constexpr (KT)
+          dma16(c.act, st + qdst[j], (rowoff[j] + k + gofs[j]) | (k + gofs[j] < uint32_t(c.k_bytes) ? 0u : kOutOfRange));
+        else
+          dma16s(c.act, st + qdst[j], rowoff[j] | gofs[j], k);     // whole K blocks: no row-end check
       }
     }
   };
@@ -683,11 +694,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
       else if (nb <= 2) gemm_item_w8<2>(p, c, lds, mt, nt);
       else if (nb <= 4) gemm_item_w8<4>(p, c, lds, mt, nt);
       else gemm_item_w8<8>(p, c, lds, mt, nt);
+    } else if (c.k_bytes % kRowBytes) {
+      if (nb <= 1) gemm_item<FMT, PHASE, 1, true>(p, c, lds, mt, nt);
+      else if (nb <= 2) gemm_item<FMT, PHASE, 2, true>(p, c, lds, mt, nt);
+      else if (nb <= 4) gemm_item<FMT, PHASE, 4, true>(p, c, lds, mt, nt);
+      else gemm_item<FMT, PHASE, 8, true>(p, c, lds, mt, nt);
     } else {
-      if (nb <= 1) gemm_item<FMT, PHASE, 1>(p, c, lds, mt, nt);
-      else if (nb <= 2) gemm_item<FMT, PHASE, 2>(p, c, lds, mt, nt);
-      else if (nb <= 4) gemm_item<FMT, PHASE, 4>(p, c, lds, mt, nt);
-      else gemm_item<FMT, PHASE, 8>(p, c, lds, mt, nt);
+      if (nb <= 1) gemm_item<FMT, PHASE, 1, false>(p, c, lds, mt, nt);
+      else if (nb <= 2) gemm_item<FMT, PHASE, 2, false>(p, c, lds, mt, nt);
+      else if (nb <= 4) gemm_item<FMT, PHASE, 4, false>(p, c, lds, mt, nt);
+      else gemm_item<FMT, PHASE, 8, false>(p, c, lds, mt, nt);
     }
   }
 }
