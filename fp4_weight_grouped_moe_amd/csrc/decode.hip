@@ -910,7 +910,7 @@ hipError_t launch_decode_fmt(const FusedParams& p0, int num_cus, hipStream_t str
                   f8_lds_bytes<RG>(p.m, p.topk, p.cap_blocks) <= size_t(kF3MaxLds);
   if (p.w4a8 && !w8) {
     // (the block-scaled FC2 rounds its own slices; the bf16 fallback needs the rounding pass)
-    if (hipError_t e = launch_mxfp8_requant(p, false, stream); e != hipSuccess) return e;
+    if (hipError_t e = launch_mxfp8_requant(p, stream); e != hipSuccess) return e;
     if (marks) marks->after(stream, KID_REQUANT);
   }
   if (split) {

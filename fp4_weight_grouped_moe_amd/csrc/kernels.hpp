@@ -147,8 +147,8 @@ bool decode_fc1_packs(const PreparedGeom& g, int64_t m, int topk);
 hipError_t launch_gemm(const FusedParams& p, int num_cus, hipStream_t stream, LaunchMarks* marks);
 // out = bf16 of the sum of each token's valid route rows y[route] (route order).
 void launch_combine(const FusedParams& p, hipStream_t stream);
-// W4A8: every valid intermediate row rounded to MXFP8 (between FC1 and FC2): as the exact
-// values in the bf16 rows, or (codes = true) as E4M3 codes and E8M0 scale bytes.
-hipError_t launch_mxfp8_requant(const FusedParams& p, bool codes, hipStream_t stream);
+// W4A8, decode path's bf16 fallback FC2: every valid intermediate row rounded to MXFP8 (between
+// FC1 and FC2), stored as the exact values in the bf16 rows.
+hipError_t launch_mxfp8_requant(const FusedParams& p, hipStream_t stream);
 
 }  // namespace moe

@@ -7,9 +7,10 @@
 // rounded to nearest, ties to even. Each valid intermediate row (fp32, slot order, written by
 // FC1 without the router weight) is rounded and stored as the exact values of its codes into
 // the bf16 rows FC2 reads: an E4M3 value times a power of two has at most 4 significant bits,
-// so bf16 holds it exactly and FC2 multiplies exactly the MXFP8 operand. For the decode path's
-// block-scaled FC2 the pass stores the codes themselves (E4M3 bytes) and one E8M0 byte per
-// group instead.
+// so bf16 holds it exactly and FC2 multiplies exactly the MXFP8 operand on the bf16 MFMA. Only
+// the decode path's fallback FC2 (routes whose K slices do not fit in its LDS) uses this pass:
+// elsewhere the rounding happens inside FC1's epilogue or FC2's staging, to E4M3 codes for the
+// block-scaled MFMA.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -22,14 +23,10 @@ namespace {
 
 constexpr int kRequantThreads = 256;
 
-// Lane l of a wave holds columns 8 l .. 8 l + 7 of a 512-column slice (fp32 in, bf16 or codes
-// out); lanes 4 g .. 4 g + 3 hold MX group g of the slice, so the group maximum is two xor
-// shuffles.
-template <bool CODES>
+// Lane l of a wave holds columns 8 l .. 8 l + 7 of a 512-column slice (fp32 in, bf16 out);
+// lanes 4 g .. 4 g + 3 hold MX group g of the slice, so the group maximum is two xor shuffles.
 __global__ __launch_bounds__(kRequantThreads) void mxfp8_requant_kernel(const float* __restrict__ inter32,
-                                                                        uint16_t* __restrict__ inter,
-                                                                        uint8_t* __restrict__ inter8,
-                                                                        uint8_t* __restrict__ sc8, int64_t ip,
+                                                                        uint16_t* __restrict__ inter, int64_t ip,
                                                                         const int32_t* __restrict__ sorted_route_ids,
                                                                         const int32_t* __restrict__ live) {
   const int rows = live[1];                                  // padded slots of this call
@@ -55,46 +52,31 @@ __global__ __launch_bounds__(kRequantThreads) void mxfp8_requant_kernel(const fl
       amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
       const int e = amax > 0.f ? mx8_exponent(amax) : 0;
-      if constexpr (CODES) {
-        uint32_t w[2] = {0u, 0u};
+      u32x4 o;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          w[i / 4] |= (amax > 0.f ? e4m3_code(e4m3_rne(ldexpf(f[i], -e))) : 0u) << (8 * (i % 4));
-        if (in) {
-          *reinterpret_cast<uint2*>(inter8 + r * ip + 8 * c) = make_uint2(w[0], w[1]);
-          if ((lane & 3) == 0) sc8[r * (ip / 32) + c / 4] = uint8_t(amax > 0.f ? e + 127 : 0);
+      for (int i = 0; i < 4; ++i) {
+        uint32_t h[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float q = amax > 0.f ? ldexpf(e4m3_rne(ldexpf(f[2 * i + j], -e)), e) : 0.f;
+          h[j] = __float_as_uint(q) >> 16;                   // exact: at most 4 significant bits
         }
-      } else {
-        u32x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t h[2];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float q = amax > 0.f ? ldexpf(e4m3_rne(ldexpf(f[2 * i + j], -e)), e) : 0.f;
-            h[j] = __float_as_uint(q) >> 16;                   // exact: at most 4 significant bits
-          }
-          o[i] = h[0] | (h[1] << 16);
-        }
-        if (in) *reinterpret_cast<u32x4*>(row + 8 * c) = o;
+        o[i] = h[0] | (h[1] << 16);
       }
+      if (in) *reinterpret_cast<u32x4*>(row + 8 * c) = o;
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_mxfp8_requant(const FusedParams& p, bool codes, hipStream_t stream) {
+hipError_t launch_mxfp8_requant(const FusedParams& p, hipStream_t stream) {
   // one wave per row, grid-stride over the padded slots (their count is read on the device)
   int64_t grid = (p.cap_blocks * kBlockM + 3) / 4;
   if (grid > 2048) grid = 2048;
   if (grid < 1) grid = 1;
-  if (codes)
-    hipLaunchKernelGGL(mxfp8_requant_kernel<true>, dim3(grid), dim3(kRequantThreads), 0, stream, p.inter32, p.inter,
-                       p.inter8, p.sc8, int64_t(p.g.ip), p.sorted_route_ids, p.live);
-  else
-    hipLaunchKernelGGL(mxfp8_requant_kernel<false>, dim3(grid), dim3(kRequantThreads), 0, stream, p.inter32, p.inter,
-                       p.inter8, p.sc8, int64_t(p.g.ip), p.sorted_route_ids, p.live);
+  hipLaunchKernelGGL(mxfp8_requant_kernel, dim3(grid), dim3(kRequantThreads), 0, stream, p.inter32, p.inter,
+                     int64_t(p.g.ip), p.sorted_route_ids, p.live);
   return hipGetLastError();
 }
 

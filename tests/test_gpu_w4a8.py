@@ -116,9 +116,9 @@ def test_w4a8_matches_oracle_scaled(moe, device, name, m, path):
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("m", [512, 16, 8])
 def test_w4a8_full_size_edge_every_output(moe, device, m):
-    """Full-size edge shape: m = 512 on the grouped GEMM (FC2 on the exact MXFP8 values in bf16);
-    m = 16 and 8 on the decode path (FC2 on the block-scaled FP4 x FP8 MFMA). Every token x every
-    column against the W4A8 oracle."""
+    """Full-size edge shape: m = 512 on the grouped GEMM, m = 16 and 8 on the decode path (FC2 on
+    the block-scaled FP4 x FP8 MFMA on both). Every token x every column against the W4A8
+    oracle."""
     case = full_case("edge", m, device)
     layer = make_layer(case, device, token_capacity=RP.token_capacity(m))
     _say(f"w4a8 full edge m={m}")
@@ -130,6 +130,53 @@ def test_w4a8_full_size_edge_every_output(moe, device, m):
     assert ok, f"w4a8 edge m={m}: {err} > {bound}"
     del layer, case
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("act", ["relu2", "silu_swiglu"])
+@pytest.mark.parametrize("path,m", [("decode", 5), ("decode", 16), ("gemm", 40), ("gemm", 512)])
+def test_w4a8_both_activations(moe, device, act, path, m):
+    """Both activations on both paths: with relu2 a grouped-GEMM wave holds whole MX groups in
+    its FC1 epilogue, with SiLU-SwiGLU two waves exchange their halves' maxima; m = 512 puts
+    ~150 routes on each of the 8 local experts (full 8-block tiles). Every output against the
+    oracle's W4A8 forward, and a second call equal to the first."""
+    import dataclasses
+    cfg = dataclasses.replace(C.get_config("edge"), num_experts=8, num_global_experts=16, hidden=512, inter=384,
+                              act=act, name=f"edge_w4a8_{act}")
+    _say(f"w4a8 {act} m={m} path={path}")
+    case = make_case(cfg, m, seed=m * 3 + len(act), weights="normal")
+    layer = make_layer(case, device)
+    moe.moe_w4a16_set_path(path)
+    try:
+        got = bf16_tensor_to_f64(run_layer(layer, case, device, w4a8=True))
+        again = bf16_tensor_to_f64(run_layer(layer, case, device, w4a8=True))
+    finally:
+        moe.moe_w4a16_set_path("auto")
+    assert np.array_equal(got, again)
+    ok, err, bound = M.within_tolerance(got, oracle_out(case, mxfp8=True))
+    _say(f"  max|err| = {err:.3e}, bound = {bound:.3e}")
+    assert ok, f"w4a8 {act} m={m} {path}: {err} > {bound}"
+
+
+@pytest.mark.parametrize("topk", [8, 16])
+def test_w4a8_decode_fallback_many_routes(moe, device, topk):
+    """More than 128 routes on the decode path (m = 12 at top-16): the K-split FC2 cannot stage
+    every route's slice, so the rounding pass writes the exact MXFP8 values as bf16 rows for the
+    one-pass FC2; at top-8 (96 routes) the block-scaled FC2 runs. Against the W4A8 oracle."""
+    import dataclasses
+    cfg = dataclasses.replace(C.get_config("edge"), num_experts=32, num_global_experts=64, hidden=512, inter=256,
+                              topk=topk, name=f"edge_w4a8_top{topk}")
+    m = 12
+    _say(f"w4a8 decode top{topk} m={m}")
+    case = make_case(cfg, m, seed=700 + topk, weights="normal")
+    layer = make_layer(case, device)
+    moe.moe_w4a16_set_path("decode")
+    try:
+        got = bf16_tensor_to_f64(run_layer(layer, case, device, w4a8=True))
+    finally:
+        moe.moe_w4a16_set_path("auto")
+    ok, err, bound = M.within_tolerance(got, oracle_out(case, mxfp8=True))
+    _say(f"  max|err| = {err:.3e}, bound = {bound:.3e}")
+    assert ok, f"w4a8 top{topk} m={m}: {err} > {bound}"
 
 
 def test_w4a8_rejects_nvfp4(moe, device):
