@@ -22,6 +22,8 @@
 //    deterministic, no atomics on data.
 //  * FC2 (one pass, when the staged rows do not fit): a workgroup (16 waves) owns 16 hidden
 //    rows for every route block and full K, with the same per-token LDS sums.
+//  * W4A8 (MXFP4 weights): the K-split FC2 rounds the staged slice of every route from FC1's
+//    fp32 rows to MXFP8 itself and runs the block-scaled FP4 x FP8 MFMA on the codes.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"

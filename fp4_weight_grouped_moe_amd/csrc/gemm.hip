@@ -8,16 +8,18 @@
 //
 // Items are (M tile, N tile) pairs: an M tile is up to 8 route blocks (128 rows) of one
 // expert, an N tile 16 row groups (256 weight rows). One 8-wave workgroup per CU, two waves
-// per SIMD: a wave's dequantisation (VALU) overlaps the other wave's MFMAs -- one wave alone
-// cannot overlap its own. The tile's activation K blocks stream through a ring of LDS stages
-// filled by buffer loads that write LDS directly; each wave streams its own two row groups'
-// E2M1 fragments and scales into a register ring of the same depth, dequantises them in
-// registers into MFMA A operands and reads activation fragments (B operands) from the stage.
+// per SIMD, so that one wave's waits on loads and LDS reads are covered by the other's MFMAs
+// (VALU issue still takes matrix-core time on gfx950: each wave's dequantisation is kept to
+// about one VALU op per MFMA). The tile's activation K blocks stream through a ring of LDS
+// stages filled by buffer loads that write LDS directly; each wave streams its own two row
+// groups' E2M1 fragments and scales into a register ring of the same depth, dequantises them
+// in registers into MFMA A operands and reads activation fragments (B operands) from the stage.
 //  * FC1 epilogue: expert FC1 global scale, SiLU-SwiGLU (gate and up fragments sit in the
 //    same lanes) or relu2, times router weight and the expert's FC2 global scale, bf16 store
-//    into the intermediate row of the route's slot.
+//    into the intermediate row of the route's slot (W4A8: rounded to MXFP8 codes instead).
 //  * FC2 epilogue: the weighted row of each route rounded to bf16; the combine pass sums each
-//    token's top-k rows in a fixed order (deterministic, no atomics) and casts to bf16.
+//    token's top-k rows in fp32 in a fixed order (deterministic, no atomics) and casts to bf16.
+//  * W4A8 FC2: the block-scaled FP4 x FP8 MFMA on FC1's MXFP8 codes (gemm_item_w8).
 // NVFP4 FC1 runs on f16 operands: activations pre-scaled per token by a power of two, E2M1 x
 // E4M3 products exact in f16 (half the dequantisation work of the bf16 route).
 #include <hip/hip_runtime.h>
