@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--flush", default="read", choices=["read", "write"],
                     help="cold protocol: read (default) or write 512 MiB of scratch between calls")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fmt", default=None, choices=["nvfp4", "mxfp4"],
+                    help="weight format override of the workload (e.g. the prefill shape with MXFP4 weights, "
+                         "to compare --w4a8 with W4A16 where FC2 is MFMA-bound)")
     ap.add_argument("--w4a8", action="store_true",
                     help="time the W4A8 variant (moe_w4a8_fused, MXFP4 workloads): whole-layer time only")
     ap.add_argument("--atomic-bf16", action="store_true",
@@ -393,6 +396,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = C.get_config(args.workload)
+    if args.fmt and args.fmt != cfg.fmt:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, fmt=args.fmt, name=f"{cfg.name}_{args.fmt}")
     m = args.m or (8 if args.workload == "decode" else max(cfg.ms))
 
     layer = Layer(moe, cfg, dev)
