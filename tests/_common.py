@@ -98,15 +98,19 @@ def oracle_out(case: Case, tokens=None, cols=None, mxfp8: bool = False) -> np.nd
     return out
 
 
-def full_case(name: str, m: int, device, codes_dev: Optional[dict] = None) -> Case:
+def full_case(name: str, m: int, device, codes_dev: Optional[dict] = None, fmt: Optional[str] = None) -> Case:
     """A full-size workload case: routing and activations seeded per (workload, m), random
-    canonical codes drawn on the device (seed per workload) unless ``codes_dev`` is given."""
+    canonical codes drawn on the device (seed per workload) unless ``codes_dev`` is given.
+    ``fmt`` overrides the workload's weight format (same shape and routing)."""
+    import dataclasses
     cfg = C.get_config(name)
+    if fmt is not None and fmt != cfg.fmt:
+        cfg = dataclasses.replace(cfg, fmt=fmt, name=f"{name}_{fmt}")
     seed = cfg.index * 1000 + m
     case = make_case(cfg, m, seed=seed, weights="none")
     case.codes_dev = codes_dev if codes_dev is not None else D.draw_random_codes_torch(cfg, seed=1000 + cfg.index,
                                                                                          device=device)
-    case.key = (name, m, seed, 1000 + cfg.index)
+    case.key = (cfg.name, m, seed, 1000 + cfg.index)
     return case
 
 

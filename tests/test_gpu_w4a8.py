@@ -132,6 +132,25 @@ def test_w4a8_full_size_edge_every_output(moe, device, m):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(900)
+def test_w4a8_full_size_prefill_mxfp4_every_output(moe, device):
+    """The prefill shape (256 experts, hidden 7168, inter 2048, top-8, Zipf routing, m = 2048)
+    with MXFP4 weights: the grouped GEMM's MXFP8-rounding FC1 epilogue and block-scaled FC2 over
+    full 8-block tiles, 16 / 28 N tiles per M tile and the per-XCD queues. Every token x every
+    column against the W4A8 oracle; W4A16 on the same layer differs (the rounding is applied)."""
+    case = full_case("prefill", 2048, device, fmt="mxfp4")
+    layer = make_layer(case, device)
+    _say("w4a8 full prefill mxfp4 m=2048")
+    got = bf16_tensor_to_f64(run_layer(layer, case, device, w4a8=True))
+    assert np.all(np.isfinite(got))
+    ref = oracle_out(case, mxfp8=True)
+    ok, err, bound = M.within_tolerance(got, ref)
+    _say(f"  w4a8 prefill mxfp4: max|err| = {err:.3e}, bound = {bound:.3e}")
+    assert ok, f"w4a8 prefill mxfp4: {err} > {bound}"
+    del layer, case
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("act", ["relu2", "silu_swiglu"])
 @pytest.mark.parametrize("path,m", [("decode", 5), ("decode", 16), ("gemm", 40), ("gemm", 512)])
 def test_w4a8_both_activations(moe, device, act, path, m):
