@@ -341,6 +341,7 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   rp.x = x;
   rp.x16 = convert ? reinterpret_cast<uint16_t*>(ws + fg.off_x16) : nullptr;
   rp.xexp = convert ? reinterpret_cast<int32_t*>(ws + fg.off_xexp) : nullptr;
+  rp.xss = convert ? reinterpret_cast<float*>(ws + fg.off_xss) : nullptr;
   rp.hidden = dims->hidden;
 
   FusedParams fp{};
@@ -366,6 +367,9 @@ int fused_impl(const moe_w4a16_dims* dims, const void* prepared, size_t prepared
   fp.inter = reinterpret_cast<uint16_t*>(ws + fg.off_inter);
   fp.x16 = rp.x16;
   fp.xexp = rp.xexp;
+  fp.xss = rp.xss;
+  fp.n13 = reinterpret_cast<const float*>(pw + g.off_n13);
+  fp.sexp = reinterpret_cast<int32_t*>(ws + fg.off_sexp);
   fp.y = reinterpret_cast<uint16_t*>(ws + fg.off_y);
   fp.part = reinterpret_cast<float*>(ws + fg.off_part);
   fp.f2_count = decode ? reinterpret_cast<int32_t*>(ws + fg.off_count) : nullptr;

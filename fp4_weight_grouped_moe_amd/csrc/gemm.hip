@@ -72,6 +72,42 @@ __device__ __forceinline__ void store_row4(uint16_t* dst, const f32x4& v) {
   *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 
+// Four consecutive values of an intermediate row times 2^-q, rounded to f16.
+__device__ __forceinline__ void store_f16x4(uint16_t* dst, const float* v, int q) {
+  const f16x2 a = f16x2{(_Float16)ldexpf(v[0], -q), (_Float16)ldexpf(v[1], -q)};
+  const f16x2 b = f16x2{(_Float16)ldexpf(v[2], -q), (_Float16)ldexpf(v[3], -q)};
+  *reinterpret_cast<uint2*>(dst) = make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+}
+
+__device__ __forceinline__ f32x4 ldexp4(const f32x4& a, int q) {
+  return f32x4{ldexpf(a[0], q), ldexpf(a[1], q), ldexpf(a[2], q), ldexpf(a[3], q)};
+}
+
+// Exponent q of a route's f16 intermediate row on the NVFP4 grouped GEMM. FC1 output j of the
+// route is a_j = g13 <x, W_j> (u_j likewise with the up rows); by Cauchy-Schwarz
+// |a_j| <= |g13| |x| n_gate and |u_j| <= |g13| |x| n_up, where |x|^2 = xss 2^(2 px) (xss: the
+// sum of squares of the token's f16 row scaled by 2^-px), and |silu(a)| <= |a|. So every value
+// of the row, silu(a) u w g2 (relu2: max(a, 0)^2 w g2), is below
+// B = g13^2 xss 2^(2 px) n_gate n_up |w g2|. Each factor is m 2^e with 1/2 <= m < 1, so
+// 2^(E-7) <= B < 2^E with E the sum of the exponents, and q = E - 14 keeps every value below
+// 2^14 (a quarter of the f16 range, ample for the fp32 rounding of the factors): nothing
+// overflows, and each value is stored within 2^-11 of itself plus 2^-25 2^q <= 2^-32 B (bf16:
+// 2^-9 of itself; on real data B exceeds the row maximum by about the reduction length). A
+// zero factor (a zero row or weight) or a non-finite one gives q = 0.
+__device__ __forceinline__ int f16_row_exponent(float g13, float xss, int px, float n_gate, float n_up, float w,
+                                                float g2) {
+  const float f[6] = {g13, xss, n_gate, n_up, w, g2};
+  int e_sum = 2 * px;
+  bool finite = true;
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const float a = fabsf(f[i]);
+    finite = finite && a > 0.f && a <= 3.4028235e38f;
+    e_sum += (i == 0 ? 2 : 1) * __builtin_amdgcn_frexp_expf(a);
+  }
+  return finite ? e_sum - 14 : 0;
+}
+
 // Per-launch constants shared by every item of a workgroup.
 struct GemmCtx {
   int groups, kbs;
@@ -119,7 +155,9 @@ template <int FMT, int PHASE, int NB, bool KT>
 __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c, uint8_t* lds, int mt, int nt) {
   using P = Plan<NB>;
   constexpr int D = P::kDepth, FR = P::FR, BW = P::BW, XD = P::XD;
-  constexpr bool F16 = FMT == FMT_NVFP4 && PHASE == 1;
+  // NVFP4 runs on f16 operands in both GEMMs: FC1 on the per-token scaled activations, FC2 on
+  // the intermediate rows that FC1 stores as f16 times a per-slot power of two.
+  constexpr bool F16 = FMT == FMT_NVFP4;
   using Dq = Deq<FMT, F16>;
   using T = typename Dq::T;
   const PreparedGeom& g = p.g;
@@ -359,16 +397,40 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
   }
   if (PHASE == 1) {
     const float g13 = p.g13[e], g2 = p.g2[e];
+    const float n_gate = F16 ? p.n13[2 * e] : 0.f, n_up = F16 ? p.n13[2 * e + 1] : 0.f;
+    // The per-route values, loaded all together first (one round trip for the slots, one for
+    // their tokens' exponents and sums of squares) from clamped addresses, so that no load is
+    // predicated and none waits behind another.
+    int2 info[BW];
+#pragma unroll
+    for (int bb = 0; bb < BW; ++bb) info[bb] = p.slot_info[(fb + min(bb, nb - 1)) * kBlockM + col];
+    int xe[BW];
+    float xs[BW];
+    if constexpr (F16) {
+#pragma unroll
+      for (int bb = 0; bb < BW; ++bb) {
+        const int t = max(info[bb].x, 0);
+        xe[bb] = p.xexp[t];
+        xs[bb] = p.xss[t];
+      }
+    }
 #pragma unroll
     for (int bb = 0; bb < BW; ++bb) {
       const int b = bb;
       if (b < nb) {
         const int64_t slot = (fb + b) * kBlockM + col;
-        const int2 info = p.slot_info[slot];
-        const bool valid = info.x >= 0;
+        const bool valid = info[bb].x >= 0;
         // W4A8: the router weight and FC2 global scale come after FC2 (outside the quantisation)
-        const float rw = valid ? (p.w4a8 ? 1.f : __int_as_float(info.y) * g2) : 0.f;
-        const float s13 = F16 && valid ? ldexpf(g13, p.xexp[info.x]) : g13;
+        const float rw = valid ? (p.w4a8 ? 1.f : __int_as_float(info[bb].y) * g2) : 0.f;
+        float s13 = g13;
+        // f16 rows: the route's row times 2^-q, q from a bound on the row (the same in every N
+        // tile of the route, so FC2 undoes it with one multiply per route)
+        int q = 0;
+        if constexpr (F16) {
+          s13 = valid ? ldexpf(g13, xe[bb]) : g13;
+          q = valid ? f16_row_exponent(g13, xs[bb], xe[bb], n_gate, n_up, __int_as_float(info[bb].y), g2) : 0;
+          if (nt == 0 && wave == 0 && r0 == 0) p.sexp[slot] = q;
+        }
         if (g.act == ACT_SWIGLU) {
 #pragma unroll
           for (int pr = 0; pr < FR / 2; ++pr) {
@@ -378,7 +440,8 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
               for (int i = 0; i < 4; ++i)
                 v[i] = silu_f32(acc[2 * pr][bb][i] * s13) * (acc[2 * pr + 1][bb][i] * s13) * rw;
               const int64_t icol = int64_t((rg_base + 2 * pr) >> 1) * 16 + r0;
-              store_inter4(p, slot, icol, v);
+              if constexpr (F16) store_f16x4(p.inter + slot * g.ip + icol, v, q);
+              else store_inter4(p, slot, icol, v);
             }
           }
         } else {
@@ -392,7 +455,8 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
                 v[i] = u * u * rw;
               }
               const int64_t icol = int64_t(rg_base + f) * 16 + r0;
-              store_inter4(p, slot, icol, v);
+              if constexpr (F16) store_f16x4(p.inter + slot * g.ip + icol, v, q);
+              else store_inter4(p, slot, icol, v);
             }
           }
         }
@@ -408,30 +472,42 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
       if (b < nb) {
         const int tok = p.slot_info[(fb + b) * kBlockM + col].x;
         if (tok >= 0) {
+          const int q = F16 ? p.sexp[(fb + b) * kBlockM + col] : 0;
 #pragma unroll
           for (int f = 0; f < FR; ++f) {
             const int64_t h = int64_t(rg_base + f) * 16 + r0;
             if (h < g.H) {
+              f32x4 a = acc[f][bb];
+              if constexpr (F16) a = ldexp4(a, q);
               bf16x2* dst = reinterpret_cast<bf16x2*>(p.out + int64_t(tok) * g.H + h);
-              __builtin_amdgcn_global_atomic_fadd_v2bf16(dst, __builtin_bit_cast(bf16x2, pack_bf16x2(acc[f][bb][0], acc[f][bb][1])));
-              __builtin_amdgcn_global_atomic_fadd_v2bf16(dst + 1, __builtin_bit_cast(bf16x2, pack_bf16x2(acc[f][bb][2], acc[f][bb][3])));
+              __builtin_amdgcn_global_atomic_fadd_v2bf16(dst, __builtin_bit_cast(bf16x2, pack_bf16x2(a[0], a[1])));
+              __builtin_amdgcn_global_atomic_fadd_v2bf16(dst + 1, __builtin_bit_cast(bf16x2, pack_bf16x2(a[2], a[3])));
             }
           }
         }
       }
     }
   } else {
+    // (route ids and row exponents loaded together first, as in FC1's epilogue)
+    int rid[BW], qv[BW];
+#pragma unroll
+    for (int bb = 0; bb < BW; ++bb) {
+      const int64_t slot = (fb + min(bb, nb - 1)) * kBlockM + col;
+      rid[bb] = p.sorted_route_ids[slot];
+      qv[bb] = F16 ? p.sexp[slot] : 0;
+    }
 #pragma unroll
     for (int bb = 0; bb < BW; ++bb) {
       const int b = bb;
       if (b < nb) {
-        const int r = p.sorted_route_ids[(fb + b) * kBlockM + col];
+        const int r = rid[bb];
         if (r >= 0) {
           const float wt = p.w4a8 ? __int_as_float(p.slot_info[(fb + b) * kBlockM + col].y) * p.g2[e] : 1.f;
+          const int q = qv[bb];
 #pragma unroll
           for (int f = 0; f < FR; ++f) {
             const int64_t h = int64_t(rg_base + f) * 16 + r0;
-            if (h < g.H) store_row4(p.y + int64_t(r) * g.H + h, acc[f][bb] * wt);
+            if (h < g.H) store_row4(p.y + int64_t(r) * g.H + h, F16 ? ldexp4(acc[f][bb], q) : acc[f][bb] * wt);
           }
         }
       }

@@ -30,6 +30,7 @@ struct RoutePackParams {
   const uint16_t* x;             // bf16 [m, hidden]
   uint16_t* x16;                 // f16 [m, hidden]
   int32_t* xexp;                 // [m] exponent p: x = x16 * 2^p
+  float* xss;                    // [m] sum of squares of each f16 row (x16), or null
   int64_t hidden;
 };
 
@@ -85,9 +86,13 @@ struct FusedParams {
   float* inter32;                // W4A8, decode path: fp32 [cap_routes, ip] activation output of FC1
   uint8_t* inter8;               // W4A8: MXFP8 codes [cap_routes, ip] (E4M3)
   uint8_t* sc8;                  //   and their E8M0 scales [cap_routes, ip / 32]
-  uint16_t* inter;               // bf16 [cap_routes, ip]
+  uint16_t* inter;               // [cap_routes, ip] bf16 (NVFP4 grouped GEMM: f16, the row times 2^-sexp)
   const uint16_t* x16;           // f16 [m, H] scaled activations (NVFP4 f16 MFMA route)
   const int32_t* xexp;           // [m] their per-token exponents
+  const float* xss;              // [m] sums of squares of the f16 rows
+  const float* n13;              // [E][2] FC1 gate / up row-norm bounds (prepared buffer)
+  int32_t* sexp;                 // [cap_routes] NVFP4 grouped GEMM: exponent q of each slot's
+                                 // f16 intermediate row (the row = inter * 2^q)
   uint16_t* y;                   // bf16 [m * topk, H] weighted FC2 rows per route (grouped GEMM)
   float* part;                   // fp32 [K splits, m, H] FC2 partial sums (decode)
   int32_t* f2_count;             // [n2_groups] FC2 K-split arrival counts (decode)

@@ -23,7 +23,8 @@ __host__ __device__ constexpr inline int64_t round_up(int64_t a, int64_t b) { re
 __host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ constexpr inline size_t align256(size_t a) { return (a + 255) & ~size_t(255); }
 
-// Prepared weights. Region order: FC1 nibbles, FC1 scales, FC2 nibbles, FC2 scales, g13, g2.
+// Prepared weights. Region order: FC1 nibbles, FC1 scales, FC2 nibbles, FC2 scales, g13, g2,
+// FC1 row-norm bounds.
 //  FC1 nibbles [E][n1_groups][hp/128][64 lanes][16 B]; lane l of a block holds, in dword s
 //  (s = 0..3), the 8 codes of row 16*rg + l%16 at K = 128*kb + 32*s + 8*(l/16) + j, code j
 //  in bits 4j..4j+3 -- exactly the A/B operand order of a 16x16x32 MFMA step s.
@@ -31,6 +32,9 @@ __host__ __device__ constexpr inline size_t align256(size_t a) { return (a + 255
 //    NVFP4: 512 B = [h 2][row 16][kb%4][s 4], byte = scale of group 8*kb + 2*s + h;
 //    MXFP4: 256 B = [row 16][kb%4][s 4],     byte = scale of group 4*kb + s.
 //  SwiGLU row groups are interleaved: rg 2g = gate rows 16g.., rg 2g+1 = up rows 16g...
+//  FC1 row-norm bounds [E][2] fp32 (NVFP4; zero for MXFP4): the largest Euclidean norm of a
+//  dequantised gate row and of an up row (global scale excluded); relu2 stores its largest row
+//  norm in both.
 struct PreparedGeom {
   int32_t fmt, act, E, H, I;
   int64_t hp, ip;           // H and I rounded up to 128
@@ -39,7 +43,7 @@ struct PreparedGeom {
   int64_t kb1, kb2;         // K blocks of FC1 (hp/128) and FC2 (ip/128)
   int64_t sc_chunk_bytes;   // 512 (NVFP4) or 256 (MXFP4)
   int64_t sc1_per_group, sc2_per_group;  // scale bytes per row group
-  size_t off_nib1, off_sc1, off_nib2, off_sc2, off_g13, off_g2, total;
+  size_t off_nib1, off_sc1, off_nib2, off_sc2, off_g13, off_g2, off_n13, total;
 };
 
 __host__ __device__ inline PreparedGeom make_prepared_geom(int32_t fmt, int32_t act, int32_t E, int32_t H,
@@ -62,6 +66,7 @@ __host__ __device__ inline PreparedGeom make_prepared_geom(int32_t fmt, int32_t 
   g.off_sc2 = o;  o = align256(o + size_t(E) * g.n2_groups * g.sc2_per_group);
   g.off_g13 = o;  o = align256(o + size_t(E) * 4);
   g.off_g2 = o;   o = align256(o + size_t(E) * 4);
+  g.off_n13 = o;  o = align256(o + size_t(E) * 8);
   g.total = o;
   return g;
 }
@@ -106,13 +111,15 @@ constexpr int kDecodeStageBytes = 131072; // LDS for the decode FC1 staged activ
 inline int64_t decode_x_pitch(const PreparedGeom& g) { return (g.hp + 511) / 512 * 512; }
 inline bool decode_stages_x(const PreparedGeom& g, int64_t m) { return m * decode_x_pitch(g) * 2 <= kDecodeStageBytes; }
 
-// Fused-layer workspace: route pack (block 16), bf16 intermediate rows per packed slot, the
-// f16 copy of the activations with per-token exponents (NVFP4), for the grouped-GEMM path
+// Fused-layer workspace: route pack (block 16), 16-bit intermediate rows per packed slot (bf16;
+// f16 times a per-slot power of two on the NVFP4 grouped-GEMM path), the f16 copy of the
+// activations with per-token exponents and sums of squares (NVFP4), for the grouped-GEMM path
 // the bf16 FC2 row of every route, summed over top-k by the combine pass, and for the
 // decode path the fp32 FC2 partial sums of each K split with their arrival counts.
 struct FusedGeom {
   PackGeom pack;
-  size_t off_pack, off_inter, off_inter32, off_inter8, off_sc8, off_x16, off_xexp, off_y, off_part, off_count, total;
+  size_t off_pack, off_inter, off_inter32, off_inter8, off_sc8, off_x16, off_xexp, off_xss, off_sexp, off_y, off_part,
+      off_count, total;
 };
 
 __host__ __device__ inline FusedGeom make_fused_geom(const PreparedGeom& w, int64_t cap, int64_t k) {
@@ -131,6 +138,10 @@ __host__ __device__ inline FusedGeom make_fused_geom(const PreparedGeom& w, int6
   f.off_sc8 = o;    o = align256(o + (w8 ? size_t(f.pack.cap_routes) * (w.ip / 32) : 0));
   f.off_x16 = o;   o = align256(o + size_t(cap) * w.H * 2);
   f.off_xexp = o;  o = align256(o + size_t(cap) * 4);
+  // NVFP4 grouped GEMM: each f16 row's sum of squares, and the exponent of each slot's f16
+  // intermediate row
+  f.off_xss = o;   o = align256(o + size_t(cap) * 4);
+  f.off_sexp = o;  o = align256(o + size_t(f.pack.cap_routes) * 4);
   f.off_y = o;     o = align256(o + size_t(cap) * k * w.H * 2);
   // decode FC2 partial sums: one fp32 [cap, H] slab per pair of intermediate K blocks
   f.off_part = o;  o = align256(o + (cap <= kDecodeMaxM ? size_t((w.kb2 + 1) / 2) * cap * w.H * 4 : 0));

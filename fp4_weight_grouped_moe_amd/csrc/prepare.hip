@@ -2,9 +2,10 @@
 // layout (FlashInfer PR 4255, Tests: preparation is lossless and bit-identical across
 // source formats and activations; Walkthrough: layout normalisation, scale packing and
 // the W13 rotation, read here as interleaving gate and up row groups). Runs once per
-// weight load; it is a byte shuffle and carries no arithmetic.
+// weight load; apart from the NVFP4 FC1 row-norm bounds it is a byte shuffle.
 #include <hip/hip_runtime.h>
 
+#include "device.hpp"
 #include "kernels.hpp"
 #include "layout.hpp"
 
@@ -122,6 +123,53 @@ __global__ void prepare_globals_kernel(PrepareParams p) {
   }
 }
 
+// NVFP4 FC1 row-norm bounds: for each expert the largest Euclidean norm of a dequantised
+// (E2M1 x E4M3, global scale excluded) gate row and of an up row; relu2 stores its largest
+// row norm in both entries. By Cauchy-Schwarz they bound every FC1 output of a token by the
+// norm of its activation row, from which the grouped GEMM picks the power of two that keeps
+// each f16 intermediate row in range. One wave per canonical row, a fixed-order sum, and the
+// maximum over rows by an integer atomic max on the non-negative fp32 bits (order-free), so
+// the bytes do not depend on scheduling.
+__global__ void prepare_norms_zero_kernel(PrepareParams p) {
+  float* n = reinterpret_cast<float*>(p.out + p.g.off_n13);
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < 2 * p.g.E; i += gridDim.x * blockDim.x) n[i] = 0.f;
+}
+
+__global__ void prepare_norms_kernel(PrepareParams p) {
+  const PreparedGeom& g = p.g;
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = g.act == ACT_SWIGLU ? 2 * int64_t(g.I) : g.I;
+  const int64_t kbytes = g.H / 2;
+  const int64_t ngroups_src = p.scale_per_row ? 1 : (g.H + 15) / 16;
+  uint32_t* n13 = reinterpret_cast<uint32_t*>(p.out + g.off_n13);
+  const int64_t waves = int64_t(gridDim.x) * (blockDim.x / 64);
+  for (int64_t w = int64_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6); w < int64_t(g.E) * rows; w += waves) {
+    const int64_t e = w / rows, row = w % rows;
+    const int64_t src = e * rows + fc1_src_row(p, row);
+    const uint8_t* codes = p.w13 + src * kbytes;
+    const uint8_t* scales = p.s13 + src * ngroups_src;
+    float ss = 0.f;
+    for (int64_t b = lane; b < kbytes; b += 64) {
+      const uint32_t c = codes[b];
+      const float sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(uint32_t(scales[p.scale_per_row ? 0 : b / 8]), 1.0f, false)[0];
+      const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);   // low code, high code
+      ss = fmaf(v[0] * sc, v[0] * sc, ss);
+      ss = fmaf(v[1] * sc, v[1] * sc, ss);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d, 64);
+    if (lane == 0) {
+      const uint32_t bits = __float_as_uint(sqrtf(ss));
+      if (g.act == ACT_SWIGLU) {
+        atomicMax(n13 + 2 * e + (row < g.I ? 0 : 1), bits);
+      } else {
+        atomicMax(n13 + 2 * e, bits);
+        atomicMax(n13 + 2 * e + 1, bits);
+      }
+    }
+  }
+}
+
 int grid_for(int64_t n, int threads) {
   int64_t b = (n + threads - 1) / threads;
   return int(b < 65536 ? (b > 0 ? b : 1) : 65536);
@@ -141,6 +189,11 @@ hipError_t launch_prepare(const PrepareParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(prepare_scales_kernel<false>, dim3(grid_for(int64_t(g.E) * g.n2_groups * g.sc2_per_group, T)),
                      dim3(T), 0, stream, p);
   hipLaunchKernelGGL(prepare_globals_kernel, dim3(grid_for(g.E, T)), dim3(T), 0, stream, p);
+  hipLaunchKernelGGL(prepare_norms_zero_kernel, dim3(grid_for(2 * int64_t(g.E), T)), dim3(T), 0, stream, p);
+  if (g.fmt == FMT_NVFP4) {
+    const int64_t rows = int64_t(g.E) * (g.act == ACT_SWIGLU ? 2 * int64_t(g.I) : g.I);
+    hipLaunchKernelGGL(prepare_norms_kernel, dim3(grid_for(rows * 64, T)), dim3(T), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

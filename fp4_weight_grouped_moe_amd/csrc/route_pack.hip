@@ -453,7 +453,8 @@ __global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParam
     return;
   }
   // One wave per activation row: row maximum, exponent p with max * 2^-p in [2^14, 2^15),
-  // then the scaled f16 row (hidden % 8 == 0: 16-byte chunks).
+  // then the scaled f16 row (hidden % 8 == 0: 16-byte chunks) and the sum of its squares (the
+  // grouped GEMM bounds each intermediate row with it).
   const int lane = threadIdx.x & 63;
   const int64_t waves = int64_t(gridDim.x - 1) * (blockDim.x / 64);
   const int chunks = int(p.hidden / 8);
@@ -475,12 +476,14 @@ __global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParam
   };
   // Each value times 2^-pexp by ldexp: a row whose maximum is below 2^-113 has pexp <= -128,
   // where the factor 2^-pexp alone would overflow to +inf.
-  auto to_f16 = [](const u32x4 v, int pexp) {
+  auto to_f16 = [](const u32x4 v, int pexp, float& ss) {
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const _Float16 lo = (_Float16)ldexpf(__uint_as_float(v[i] << 16), -pexp);
       const _Float16 hi = (_Float16)ldexpf(__uint_as_float(v[i] & 0xFFFF0000u), -pexp);
+      ss = fmaf(float(lo), float(lo), ss);
+      ss = fmaf(float(hi), float(hi), ss);
       o[i] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
     }
     return o;
@@ -505,21 +508,33 @@ __global__ __launch_bounds__(kPackThreads) void route_pack_kernel(RoutePackParam
       for (int i = 0; i < kRowRegs; ++i) amax = chunk_max(w[i], amax);
     }
     const int pexp = pexp_of(row_max(amax));
+    float ss = 0.f;       // (chunks past the row load as zeros)
     if (chunks <= 64 * kRowRegs) {
 #pragma unroll
-      for (int i = 0; i < kRowRegs; ++i)
-        if (lane + 64 * i < chunks) __builtin_amdgcn_raw_buffer_store_b128(to_f16(v[i], pexp), dst, (lane + 64 * i) * 16, 0, 0);
+      for (int i = 0; i < kRowRegs; ++i) {
+        const u32x4 o = to_f16(v[i], pexp, ss);
+        if (lane + 64 * i < chunks) __builtin_amdgcn_raw_buffer_store_b128(o, dst, (lane + 64 * i) * 16, 0, 0);
+      }
     } else {
-      for (int base = 0; base < chunks; base += 64 * kRowRegs) {
-        u32x4 w[kRowRegs];
+      // (half batches here: the full ones made the kernel spill registers)
+      constexpr int kHalf = kRowRegs / 2;
+      for (int base = 0; base < chunks; base += 64 * kHalf) {
+        u32x4 w[kHalf];
 #pragma unroll
-        for (int i = 0; i < kRowRegs; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b128(src, (base + lane + 64 * i) * 16, 0, 0);
+        for (int i = 0; i < kHalf; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b128(src, (base + lane + 64 * i) * 16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < kRowRegs; ++i)
-          if (base + lane + 64 * i < chunks) __builtin_amdgcn_raw_buffer_store_b128(to_f16(w[i], pexp), dst, (base + lane + 64 * i) * 16, 0, 0);
+        for (int i = 0; i < kHalf; ++i) {
+          const u32x4 o = to_f16(w[i], pexp, ss);
+          if (base + lane + 64 * i < chunks) __builtin_amdgcn_raw_buffer_store_b128(o, dst, (base + lane + 64 * i) * 16, 0, 0);
+        }
       }
     }
-    if (lane == 0) p.xexp[t] = pexp;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) ss += __shfl_xor(ss, d, 64);
+    if (lane == 0) {
+      p.xexp[t] = pexp;
+      if (p.xss) p.xss[t] = ss;
+    }
   }
 }
 

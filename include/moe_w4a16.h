@@ -128,7 +128,9 @@ int moe_route_pack(const int32_t* topk_ids, int64_t m, int topk, const int32_t* 
  * The prepared buffer is an opaque, lossless gfx950 layout: 16-row x 128-K fragments
  * whose nibbles each lane reads with one 128-bit load in MFMA operand order, scales
  * packed four K-blocks per 128-bit load, K and rows zero-padded to multiples of 128,
- * SwiGLU gate and up row groups interleaved. */
+ * SwiGLU gate and up row groups interleaved; with NVFP4 it also holds each expert's largest
+ * dequantised FC1 gate and up row norms, which bound the intermediate rows that the grouped
+ * GEMM keeps in f16 (see moe_w4a16_fused). */
 int moe_w4a16_prepared_size(const moe_w4a16_dims* dims, size_t* bytes);
 
 int moe_w4a16_prepare(const moe_w4a16_dims* dims, const uint8_t* w13, const uint8_t* s13,
@@ -178,7 +180,12 @@ int moe_w4a16_prepare_layout(const moe_w4a16_dims* dims, const moe_w4a16_source_
  * epilogue over (route tile, weight tile) items, FC2 writing each route's weighted row
  * rounded to bf16, and a combine pass that sums every token's top-k rows in fp32 in route
  * order and casts to bf16 -- deterministic, no atomics on data. Persistent workgroups take items from a
- * queue; no workgroup waits on another that may not be resident. */
+ * queue; no workgroup waits on another that may not be resident. The intermediate (activation
+ * output) rows are 16-bit: bf16, except on the grouped-GEMM path with NVFP4 weights, where both
+ * GEMMs run on f16 operands and each route's row is stored in f16 times a power of two chosen
+ * from a bound on the row (the token's activation norm, the expert's largest FC1 row norms, the
+ * global scales and the router weight): no value can overflow, and each is stored within
+ * 2^-11 of itself plus 2^-32 of the bound (bf16: 2^-9 of itself). */
 #define MOE_DECODE_MAX_M 16
 
 /* Workspace bytes for moe_w4a16_fused at a token capacity (route packing included). */

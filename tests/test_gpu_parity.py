@@ -436,3 +436,42 @@ def test_tiny_and_zero_activation_rows(moe, device, path):
     assert np.all(np.isfinite(got))
     assert np.all(got[5] == 0)
     _check(case, got, label=f"tiny / zero rows {path}")
+
+
+@pytest.mark.parametrize("name", ["decode_s", "small_s"])
+def test_gemm_f16_intermediate_rows_across_magnitudes(moe, device, name):
+    """The NVFP4 grouped GEMM stores each route's intermediate row as f16 times a power of two
+    chosen from a bound on the row (activation-row norm, the expert's largest FC1 row norms, the
+    global scales and the router weight). Token rows scaled by 1e-8 and 1e8, a token with router
+    weights scaled by 1e-12, and one expert's global scales moved by 2^30 (FC1) and 2^-40 (FC2):
+    every token's output row within the relative tolerance of its own largest value (SwiGLU and
+    relu2), and none of it non-finite."""
+    cfg = SCALED[name]
+    assert cfg.fmt == "nvfp4"
+    case = make_case(cfg, 24, seed=91, weights="normal")
+    x = F.bf16_bits_to_f64(case.xbits)
+    x[1] *= 1e-8
+    x[4] *= 1e8
+    case.xbits = D.bf16_bits_from_f32(x.astype(np.float32))
+    case.w = case.w.copy()
+    case.w[7] *= 1e-12
+    e0 = int(case.ids[10, 0])
+    case.codes = dict(case.codes)
+    case.codes["g13"] = case.codes["g13"].copy()
+    case.codes["g2"] = case.codes["g2"].copy()
+    case.codes["g13"][e0] *= np.float32(2.0 ** 30)
+    case.codes["g2"][e0] *= np.float32(2.0 ** -40)
+    layer = make_layer(case, device)
+    _say(f"f16 intermediate magnitudes {name} (expert {e0} rescaled)")
+    moe.moe_w4a16_set_path("gemm")
+    try:
+        got = bf16_tensor_to_f64(run_layer(layer, case, device))
+    finally:
+        moe.moe_w4a16_set_path("auto")
+    assert np.all(np.isfinite(got))
+    ref = oracle_out(case)
+    for t in range(case.m):
+        ok, err, bound = M.within_tolerance(got[t], ref[t], abs_=0.0)
+        assert ok, f"{name} token {t}: max|err| {err:.3e} > {bound:.3e} (max|ref| {np.abs(ref[t]).max():.3e})"
+    _say(f"  every row within 2e-2 of its own maximum (row maxima {np.abs(ref).max(axis=1).min():.2e} .. "
+         f"{np.abs(ref).max(axis=1).max():.2e})")
