@@ -370,11 +370,14 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
         for (int bb = 0; bb < BW; ++bb) am[bb] = fmaxf(am[bb], xam[((wave ^ 1) * BW + bb) * 16 + col]);
       }
       const int64_t ip = g.ip;
+      int tok[BW];
+#pragma unroll
+      for (int bb = 0; bb < BW; ++bb) tok[bb] = p.slot_info[(fb + min(bb, nb - 1)) * kBlockM + col].x;
 #pragma unroll
       for (int bb = 0; bb < BW; ++bb) {
         if (bb < nb && rg_base < c.groups) {
           const int64_t slot = (fb + bb) * kBlockM + col;
-          if (p.slot_info[slot].x >= 0) {
+          if (tok[bb] >= 0) {
             const float amax = am[bb];
             const int ex = amax > 0.f ? mx8_exponent(amax) : 0;
             const uint8_t sbyte = uint8_t(amax > 0.f ? ex + 127 : 0);
@@ -673,12 +676,22 @@ __device__ __forceinline__ void gemm_item_w8(const FusedParams& p, const GemmCtx
   // Epilogue: the weighted bf16 row of each route (router weight x FC2 global scale, outside
   // the quantisation), summed over top-k by the combine pass.
   const int r0 = 4 * q;
+  // (route ids and router weights of all blocks loaded together first, from clamped slots)
+  const float g2 = p.g2[e];
+  int rid[NB];
+  float rwt[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int64_t slot = (fb + min(b, nb - 1)) * kBlockM + col;
+    rid[b] = p.sorted_route_ids[slot];
+    rwt[b] = __int_as_float(p.slot_info[slot].y);
+  }
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     if (b < nb) {
-      const int r = p.sorted_route_ids[(fb + b) * kBlockM + col];
+      const int r = rid[b];
       if (r >= 0) {
-        const float wt = __int_as_float(p.slot_info[(fb + b) * kBlockM + col].y) * p.g2[e];
+        const float wt = rwt[b] * g2;
 #pragma unroll
         for (int f = 0; f < FR; ++f) {
           const int64_t hh = int64_t(rg_base + f) * 16 + r0;
