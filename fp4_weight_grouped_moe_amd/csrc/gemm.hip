@@ -48,8 +48,9 @@ struct Plan {
   static constexpr int BW = NB;                                     // route blocks per wave
   static constexpr int XD = NB >= 2 ? NB / 2 : 1;                   // activation loads per wave (NB 1: waves 4-7 repeat 0-3)
   static constexpr int kStage = NB * kBlockBytes;
-  // 3 stages for 8-block tiles (measured ~2% faster FC1 than 4: fewer ring registers), else 6
-  static constexpr int kDepth = NB == 8 ? 3 : (kLdsBytes / kStage < 6 ? kLdsBytes / kStage : 6);
+  // 3 stages for 8-block tiles (measured ~2% faster FC1 than 4: fewer ring registers), else up
+  // to 6 below the W4A8 exchange area (4 for 6-block tiles)
+  static constexpr int kDepth = NB == 8 ? 3 : (kW8AmaxOffset / kStage < 6 ? kW8AmaxOffset / kStage : 6);
   static constexpr int kLoads = XD + 2 * FR;                        // vector loads a wave issues per stage
   static_assert(kDepth >= 3 && (kDepth - 1) * kLoads < 64, "ring too shallow or vmcnt out of range");
   static_assert(XD <= 2 * FR, "the stage wait relies on at least as many register loads as LDS loads");
@@ -779,7 +780,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
     // s_item before all threads have taken it.
     const int mt = item / n_nt, nt = item % n_nt;
     const int nb = __builtin_amdgcn_readfirstlane(p.tiles[mt].y & 0xFF);
-    // Tiles are compiled for 1, 2, 4 or 8 route blocks so that the MFMA loop is straight-line.
+    // Tiles are compiled for 1, 2, 4, 6 or 8 route blocks so that the MFMA loop is straight-line
+    // (6: the W4A16 kernel only; five- and six-block tiles ran as eight, prefill FC1 -1.6 %).
     if constexpr (W8) {
       if (nb <= 1) gemm_item_w8<1>(p, c, lds, mt, nt);
       else if (nb <= 2) gemm_item_w8<2>(p, c, lds, mt, nt);
@@ -789,11 +791,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
       if (nb <= 1) gemm_item<FMT, PHASE, 1, true>(p, c, lds, mt, nt);
       else if (nb <= 2) gemm_item<FMT, PHASE, 2, true>(p, c, lds, mt, nt);
       else if (nb <= 4) gemm_item<FMT, PHASE, 4, true>(p, c, lds, mt, nt);
+      else if (nb <= 6) gemm_item<FMT, PHASE, 6, true>(p, c, lds, mt, nt);
       else gemm_item<FMT, PHASE, 8, true>(p, c, lds, mt, nt);
     } else {
       if (nb <= 1) gemm_item<FMT, PHASE, 1, false>(p, c, lds, mt, nt);
       else if (nb <= 2) gemm_item<FMT, PHASE, 2, false>(p, c, lds, mt, nt);
       else if (nb <= 4) gemm_item<FMT, PHASE, 4, false>(p, c, lds, mt, nt);
+      else if (nb <= 6) gemm_item<FMT, PHASE, 6, false>(p, c, lds, mt, nt);
       else gemm_item<FMT, PHASE, 8, false>(p, c, lds, mt, nt);
     }
   }

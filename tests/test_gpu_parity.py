@@ -438,6 +438,28 @@ def test_tiny_and_zero_activation_rows(moe, device, path):
     _check(case, got, label=f"tiny / zero rows {path}")
 
 
+@pytest.mark.parametrize("name,E,hidden,inter,m", [("edge", 4, 384, 1400, 176), ("small", 8, 384, 256, 120)])
+def test_gemm_six_block_tiles(moe, device, name, E, hidden, inter, m):
+    """Experts with 81-96 routes, whose tail M tiles run as six-block tiles on the grouped GEMM:
+    MXFP4 SwiGLU with the intermediate's K tail (I = 1400) and an expert map, and NVFP4 relu2.
+    Every output against the oracle."""
+    cfg = C.scaled(C.get_config(name), num_experts=E, hidden=hidden, inter=inter, name=f"{name}_six")
+    case = make_case(cfg, m, seed=5, weights="normal")
+    ids = case.ids[case.ids >= 0]
+    loc = case.emap[ids] if case.emap is not None else ids
+    counts = np.bincount(loc[loc >= 0], minlength=E)
+    tails = ((counts + 15) // 16) % 8
+    assert np.any((tails == 5) | (tails == 6)), counts
+    layer = make_layer(case, device)
+    _say(f"six-block tiles {name} m={m} expert loads {counts.tolist()}")
+    moe.moe_w4a16_set_path("gemm")
+    try:
+        got = bf16_tensor_to_f64(run_layer(layer, case, device))
+    finally:
+        moe.moe_w4a16_set_path("auto")
+    _check(case, got, label=f"six-block tiles {name}")
+
+
 @pytest.mark.parametrize("name", ["decode_s", "small_s"])
 def test_gemm_f16_intermediate_rows_across_magnitudes(moe, device, name):
     """The NVFP4 grouped GEMM stores each route's intermediate row as f16 times a power of two
