@@ -169,6 +169,26 @@ __global__ __launch_bounds__(kF1Threads, 1) void decode_fc1_kernel(FusedParams p
       if (lane == 0) sp[t] = pe;
     }
   };
+  // A unit's weight loads: K slice `sl` of row groups 2 it, 2 it + 1 of expert eb (fragment
+  // blocks and their scale dwords). Base addresses are wave-uniform (scalar registers); lanes
+  // add a 32-bit offset.
+  auto load_unit = [&](int eb, int it, int sl, F1Unit& r) {
+    const int64_t gi = int64_t(eb) * g.n1_groups + 2 * it;
+    const uint8_t* nb0 = p.nib1 + gi * g.kb1 * kFragBytes;
+    const uint8_t* nb1 = nb0 + g.kb1 * kFragBytes;
+#pragma unroll
+    for (int j = 0; j < kF1Slice; ++j) {
+      const int kb = min(sl * kF1Slice + j, kb1 - 1);
+      r.q0[j] = *reinterpret_cast<const u32x4*>(nb0 + int64_t(kb) * kFragBytes + lane * 16);
+      r.q1[j] = *reinterpret_cast<const u32x4*>(nb1 + int64_t(kb) * kFragBytes + lane * 16);
+    }
+    const uint8_t* sg0 = p.sc1 + gi * g.sc1_per_group + int64_t(sl) * g.sc_chunk_bytes;
+    r.s0 = *reinterpret_cast<const u32x4*>(sg0 + sc_lane);
+    r.s1 = *reinterpret_cast<const u32x4*>(sg0 + g.sc1_per_group + sc_lane);
+  };
+  F1Unit ra, rb;
+  bool early = false;          // unit 0's weight loads already issued (PACK)
+
   if constexpr (PACK) {
     // The route pack of these few routes (R <= 256, one per thread), done by every workgroup
     // in its own LDS so that no launch waits for another: local expert ids, counts, padded
@@ -208,6 +228,33 @@ __global__ __launch_bounds__(kF1Threads, 1) void decode_fc1_kernel(FusedParams p
       }
     }
     pack_barrier();
+    // The weights of each wave's first unit go out now, before the rest of the pack: with at
+    // most 64 routes (one per lane) and at most 16 routes on each of the experts up to the
+    // unit's block, that block's expert is the (block)-th smallest distinct local id, found by
+    // repeated wave minima -- the block the pack below assigns it. Otherwise the loads wait
+    // for the pack as usual. A wave that staged rows waits for them first (they left first and
+    // have landed by now), so that no later wait counts these loads.
+    {
+      const int blk0 = int(blockIdx.x) / n_it;
+      if (R <= 64 && blk0 < 8) {
+        const int li = lane < R ? int(sl[lane]) : -1;
+        int prev = -1, v = -1;
+        bool ok = true;
+        for (int k = 0; k <= blk0 && ok; ++k) {
+          int cand = li > prev ? li : INT32_MAX;
+#pragma unroll
+          for (int d = 32; d >= 1; d >>= 1) cand = min(cand, __shfl_xor(cand, d, 64));
+          v = uniform(cand);
+          ok = v != INT32_MAX && __popcll(__ballot(li == v)) <= kBlockM;
+          prev = v;
+        }
+        if (ok) {
+          early = true;
+          wait_vmcnt<0>();
+          load_unit(v, int(blockIdx.x) % n_it, min(wave, nsl - 1), ra);
+        }
+      }
+    }
     const int l = tid < kF1PackRoutes ? int(sl[tid]) : -1;
     if (l >= 0) atomicAdd(&cnt[l], 1);
     pack_barrier();
@@ -261,7 +308,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void decode_fc1_kernel(FusedParams p
     } else if (tid < R && blockIdx.x == 0) {
       p.route_slot[tid] = -1;
     }
-    wait_vmcnt<0>();                                          // the rows (waves 1..3) have landed
+    if (!early) wait_vmcnt<0>();                              // the rows (waves 1..3) have landed
     pack_barrier();
     live_blocks = total / kBlockM;
     if (blockIdx.x == 0) {
@@ -286,10 +333,10 @@ __global__ __launch_bounds__(kF1Threads, 1) void decode_fc1_kernel(FusedParams p
   const int U2 = (U + 1) & ~1;                                // even: units are taken in pairs
 
   // Loads are unconditional so that the wait counters stay exact: units past the end and
-  // K blocks past kb1 re-read a valid block (an L2 hit) whose contribution is skipped.
-  // Base addresses are wave-uniform (scalar registers); lanes add a 32-bit offset. The
-  // block's expert comes through the scalar cache, so it waits on no vector load.
-  auto issue = [&](int u, F1Unit& r) {
+  // K blocks past kb1 re-read a valid block (an L2 hit) whose contribution is skipped. The
+  // block's expert comes through the scalar cache, so it waits on no vector load. `loads`
+  // false: only the unit's route column (its loads went out early).
+  auto issue = [&](int u, F1Unit& r, bool loads = true) {
     const int uu = min(u, U - 1);
     const int item = int(blockIdx.x) + (uu / spw) * int(gridDim.x);
     const int sl = min(wave + kF1Waves * (uu % spw), nsl - 1);
@@ -303,18 +350,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void decode_fc1_kernel(FusedParams p
       r.info = p.slot_info[blk * kBlockM + col];
       eb = scalar_load(p.block_expert, blk);
     }
-    const int64_t gi = int64_t(eb) * g.n1_groups + 2 * it;
-    const uint8_t* nb0 = p.nib1 + gi * g.kb1 * kFragBytes;
-    const uint8_t* nb1 = nb0 + g.kb1 * kFragBytes;
-#pragma unroll
-    for (int j = 0; j < kF1Slice; ++j) {
-      const int kb = min(sl * kF1Slice + j, kb1 - 1);
-      r.q0[j] = *reinterpret_cast<const u32x4*>(nb0 + int64_t(kb) * kFragBytes + lane * 16);
-      r.q1[j] = *reinterpret_cast<const u32x4*>(nb1 + int64_t(kb) * kFragBytes + lane * 16);
-    }
-    const uint8_t* sg0 = p.sc1 + gi * g.sc1_per_group + int64_t(sl) * g.sc_chunk_bytes;
-    r.s0 = *reinterpret_cast<const u32x4*>(sg0 + sc_lane);
-    r.s1 = *reinterpret_cast<const u32x4*>(sg0 + g.sc1_per_group + sc_lane);
+    if (loads) load_unit(eb, it, sl, r);
   };
 
   // Two register sets: the next unit's loads stay in flight while this one is computed. The
@@ -322,8 +358,7 @@ __global__ __launch_bounds__(kF1Threads, 1) void decode_fc1_kernel(FusedParams p
   // last barrier) are converted while its weights are in flight, and only then is the second
   // unit issued: with both issued first, the conversion waited behind a full load queue and
   // held up every wave at the barrier below (m = 8: FC1 75.6 -> 73.9 us).
-  F1Unit ra, rb;
-  issue(0, ra);
+  issue(0, ra, !early);
   if constexpr (PACK && F16) convert_rows();
   issue(1, rb);
 
