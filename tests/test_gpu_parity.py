@@ -438,6 +438,32 @@ def test_tiny_and_zero_activation_rows(moe, device, path):
     _check(case, got, label=f"tiny / zero rows {path}")
 
 
+@pytest.mark.parametrize("pattern", ["smallest_expert_heavy", "middle_expert_heavy"])
+def test_decode_in_launch_pack_with_repeated_ids(moe, device, pattern):
+    """The decode FC1 launch that packs its own routes issues each wave's first unit before the
+    pack whenever the experts up to that unit's block hold at most 16 routes each. Top-k lists
+    that repeat one expert (more than 16 routes on it: two route blocks) exercise both the early
+    issue (blocks before the heavy expert) and the fallback (blocks at or after it): m = 8, every
+    output against the oracle."""
+    cfg = SCALED["decode_s"]
+    case = make_case(cfg, 8, seed=23, weights="normal")
+    ids = case.ids.copy()
+    heavy = 0 if pattern == "smallest_expert_heavy" else 9
+    ids[:3, :] = heavy                                   # 24 routes on one expert
+    if pattern == "middle_expert_heavy":
+        ids[3:, :] = np.where(ids[3:, :] == heavy, 1, ids[3:, :])
+    case.ids = ids.astype(np.int32)
+    assert (case.ids == heavy).sum() > 16
+    layer = make_layer(case, device)
+    _say(f"decode in-launch pack, {pattern}")
+    moe.moe_w4a16_set_path("decode")
+    try:
+        got = bf16_tensor_to_f64(run_layer(layer, case, device))
+    finally:
+        moe.moe_w4a16_set_path("auto")
+    _check(case, got, label=f"decode pack {pattern}")
+
+
 @pytest.mark.parametrize("name,E,hidden,inter,m", [("edge", 4, 384, 1400, 176), ("small", 8, 384, 256, 120)])
 def test_gemm_six_block_tiles(moe, device, name, E, hidden, inter, m):
     """Experts with 81-96 routes, whose tail M tiles run as six-block tiles on the grouped GEMM:
