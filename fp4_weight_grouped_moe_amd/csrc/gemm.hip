@@ -37,6 +37,7 @@ constexpr int kRowBytes = kKBlock * 2;                  // one activation row of
 constexpr int kBlockBytes = kBlockM * kRowBytes;        // one route block of a K block: 4 KiB
 constexpr int kLdsBytes = 131072;                       // the activation stage ring
 constexpr int kW8AmaxOffset = 98304;                    // W4A8 FC1 epilogue: per-wave group maxima (4 KiB)
+constexpr int kEarlyTicketKB = 32;                      // items up to this many K blocks take their successor's ticket early
 
 // Wave layout and pipeline depth for tiles of NB route blocks: the 8 waves split the N tile,
 // 2 row groups x NB blocks each, so every fragment is loaded and dequantised by exactly one
@@ -152,8 +153,9 @@ __device__ __forceinline__ f32x4 mma(const f16x8& a, const f16x8& b, const f32x4
 // One item: NB route blocks (16 NB rows) of one expert x 256 weight rows, full K.
 // KT: the activation K extent is not a multiple of the 256-byte K block (hidden size not a
 // multiple of 128): every activation load checks its lane's offset against the row end.
-template <int FMT, int PHASE, int NB, bool KT>
-__device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c, uint8_t* lds, int mt, int nt) {
+template <int FMT, int PHASE, int NB, bool KT, typename Hook>
+__device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c, uint8_t* lds, int mt, int nt,
+                                          Hook&& take_ticket) {
   using P = Plan<NB>;
   constexpr int D = P::kDepth, FR = P::FR, BW = P::BW, XD = P::XD;
   // NVFP4 runs on f16 operands in both GEMMs: FC1 on the per-token scaled activations, FC2 on
@@ -304,9 +306,14 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
   // activation rows be read before they landed). So the wait leaves at most the later
   // stages' LDS loads, (D-2) * XD, outstanding: then this stage's LDS loads have landed, and
   // so have its register loads (at least 4 (D-2) >= (D-2) * XD register loads follow them).
+  // The hook takes the next item's queue ticket: once the first stage has landed for items of
+  // up to kEarlyTicketKB K blocks (edge and small shapes -3 %), after the K loop for longer
+  // ones (taken early in a 56-block prefill FC1 item it cost 2.6 %).
+  const bool early_ticket = kbs <= kEarlyTicketKB;
   auto step = [&](int kb, int j) {
     wait_vmcnt<(D - 2) * XD>();
     stage_barrier();
+    if (kb == 0 && early_ticket) take_ticket();
     __builtin_amdgcn_sched_barrier(0);
     const int jn = (j + D - 1) % D;
     compute(j, wr[j], sc[j], kb + D - 1, jn, wr[jn], sc[jn]);
@@ -324,6 +331,7 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
     if (kb + j < kbs) step(kb + j, j);
   // Drain the stages issued past K before the slots are reused by the next item.
   wait_vmcnt<0>();
+  if (!early_ticket) take_ticket();
 
   // Epilogue. Lane (r0 = 4 (lane / 16), col = lane % 16) holds rows r0..r0+3 of each
   // 16-row group, route column col of each block.
@@ -543,8 +551,9 @@ struct PlanW8 {
   static_assert(kDepth * kStage <= kLdsBytes, "stage ring larger than the LDS");
 };
 
-template <int NB>
-__device__ __forceinline__ void gemm_item_w8(const FusedParams& p, const GemmCtx& c, uint8_t* lds, int mt, int nt) {
+template <int NB, typename Hook>
+__device__ __forceinline__ void gemm_item_w8(const FusedParams& p, const GemmCtx& c, uint8_t* lds, int mt, int nt,
+                                             Hook&& take_ticket) {
   using P = PlanW8<NB>;
   constexpr int D = P::kDepth, FR = P::FR, XD = P::XD;
   const PreparedGeom& g = p.g;
@@ -653,9 +662,11 @@ __device__ __forceinline__ void gemm_item_w8(const FusedParams& p, const GemmCtx
 
   // The same ring as the W4A16 item (loads into LDS and into registers complete in order within
   // each kind): the wait leaves only the later stages' LDS loads outstanding.
+  const bool early_ticket = kbs <= kEarlyTicketKB;    // (the next item's ticket, as in the W4A16 item)
   auto step = [&](int kb, int j) {
     wait_vmcnt<(D - 2) * P::kLds>();
     stage_barrier();
+    if (kb == 0 && early_ticket) take_ticket();
     __builtin_amdgcn_sched_barrier(0);
     const int jn = (j + D - 1) % D;
     issue(kb + D - 1, jn, wr[jn], sc[jn]);
@@ -673,6 +684,7 @@ __device__ __forceinline__ void gemm_item_w8(const FusedParams& p, const GemmCtx
   for (int j = 0; j < D - 1; ++j)
     if (kb + j < kbs) step(kb + j, j);
   wait_vmcnt<0>();
+  if (!early_ticket) take_ticket();
 
   // Epilogue: the weighted bf16 row of each route (router weight x FC2 global scale, outside
   // the quantisation), summed over top-k by the combine pass.
@@ -742,64 +754,71 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(FusedParams p) {
   // busy together. The same expert's M tiles on the other XCDs read its weight tiles at the
   // same time, which the Infinity Cache serves. An exhausted queue sends a workgroup on to
   // the next one, so the load stays balanced to the end.
-  __shared__ int s_item;
   int* queues = p.live + (PHASE == 1 ? 8 : 16);
   const int n_full = p.live[5], n_part = n_mt - n_full;
   int q = blockIdx.x & 7, tried = 0;                 // thread 0's queue cursor
-  for (;;) {
-    if (threadIdx.x == 0) {
-      int found = -1;
-      while (tried < 8) {
-        const int fq = n_full > q ? (n_full - 1 - q) / 8 + 1 : 0;
-        const int pq = n_part > q ? (n_part - 1 - q) / 8 + 1 : 0;
-        const int i = atomicAdd(&queues[q], 1);
-        if (i < (fq + pq) * n_nt) {
-          const int m = i / n_nt, both = min(fq, pq);
-          bool full;
-          int ord;
-          if (m < 2 * both) {
-            full = (m & 1) == 0;
-            ord = m >> 1;
-          } else {
-            full = fq > pq;
-            ord = m - both;
-          }
-          const int mt = full ? q + 8 * ord : n_full + q + 8 * ord;
-          found = mt * n_nt + i % n_nt;
-          break;
+  // Thread 0: the item that ticket i of queue q stands for, or, when that queue is exhausted,
+  // the next queue's (one more ticket each, -1 when every queue is).
+  auto take = [&](int i) {
+    for (;;) {
+      const int fq = n_full > q ? (n_full - 1 - q) / 8 + 1 : 0;
+      const int pq = n_part > q ? (n_part - 1 - q) / 8 + 1 : 0;
+      if (i < (fq + pq) * n_nt) {
+        const int m = i / n_nt, both = min(fq, pq);
+        bool full;
+        int ord;
+        if (m < 2 * both) {
+          full = (m & 1) == 0;
+          ord = m >> 1;
+        } else {
+          full = fq > pq;
+          ord = m - both;
         }
-        q = (q + 1) & 7;
-        ++tried;
+        const int mt = full ? q + 8 * ord : n_full + q + 8 * ord;
+        return mt * n_nt + i % n_nt;
       }
-      s_item = found;
+      q = (q + 1) & 7;
+      if (++tried == 8) return -1;
+      i = atomicAdd(&queues[q], 1);
     }
-    lds_barrier();
-    const int item = __builtin_amdgcn_readfirstlane(s_item);
+  };
+  // The next item's ticket is taken while the current item runs (see gemm_item), so that its
+  // round trip is off the path between items; s_item alternates between the current item and
+  // the one taken during it.
+  __shared__ int s_item[2];
+  if (threadIdx.x == 0) s_item[0] = take(atomicAdd(&queues[q], 1));
+  lds_barrier();
+  for (int par = 0;; par ^= 1) {
+    const int item = __builtin_amdgcn_readfirstlane(s_item[par]);
     if (item < 0) break;
-    // Every item starts with a barrier after this read, so thread 0 cannot overwrite
-    // s_item before all threads have taken it.
+    int ticket = 0;
+    auto reserve = [&]() {
+      if (threadIdx.x == 0 && tried < 8) ticket = atomicAdd(&queues[q], 1);
+    };
     const int mt = item / n_nt, nt = item % n_nt;
     const int nb = __builtin_amdgcn_readfirstlane(p.tiles[mt].y & 0xFF);
     // Tiles are compiled for 1, 2, 4, 6 or 8 route blocks so that the MFMA loop is straight-line
     // (6: the W4A16 kernel only; five- and six-block tiles ran as eight, prefill FC1 -1.6 %).
     if constexpr (W8) {
-      if (nb <= 1) gemm_item_w8<1>(p, c, lds, mt, nt);
-      else if (nb <= 2) gemm_item_w8<2>(p, c, lds, mt, nt);
-      else if (nb <= 4) gemm_item_w8<4>(p, c, lds, mt, nt);
-      else gemm_item_w8<8>(p, c, lds, mt, nt);
+      if (nb <= 1) gemm_item_w8<1>(p, c, lds, mt, nt, reserve);
+      else if (nb <= 2) gemm_item_w8<2>(p, c, lds, mt, nt, reserve);
+      else if (nb <= 4) gemm_item_w8<4>(p, c, lds, mt, nt, reserve);
+      else gemm_item_w8<8>(p, c, lds, mt, nt, reserve);
     } else if (c.k_bytes % kRowBytes) {
-      if (nb <= 1) gemm_item<FMT, PHASE, 1, true>(p, c, lds, mt, nt);
-      else if (nb <= 2) gemm_item<FMT, PHASE, 2, true>(p, c, lds, mt, nt);
-      else if (nb <= 4) gemm_item<FMT, PHASE, 4, true>(p, c, lds, mt, nt);
-      else if (nb <= 6) gemm_item<FMT, PHASE, 6, true>(p, c, lds, mt, nt);
-      else gemm_item<FMT, PHASE, 8, true>(p, c, lds, mt, nt);
+      if (nb <= 1) gemm_item<FMT, PHASE, 1, true>(p, c, lds, mt, nt, reserve);
+      else if (nb <= 2) gemm_item<FMT, PHASE, 2, true>(p, c, lds, mt, nt, reserve);
+      else if (nb <= 4) gemm_item<FMT, PHASE, 4, true>(p, c, lds, mt, nt, reserve);
+      else if (nb <= 6) gemm_item<FMT, PHASE, 6, true>(p, c, lds, mt, nt, reserve);
+      else gemm_item<FMT, PHASE, 8, true>(p, c, lds, mt, nt, reserve);
     } else {
-      if (nb <= 1) gemm_item<FMT, PHASE, 1, false>(p, c, lds, mt, nt);
-      else if (nb <= 2) gemm_item<FMT, PHASE, 2, false>(p, c, lds, mt, nt);
-      else if (nb <= 4) gemm_item<FMT, PHASE, 4, false>(p, c, lds, mt, nt);
-      else if (nb <= 6) gemm_item<FMT, PHASE, 6, false>(p, c, lds, mt, nt);
-      else gemm_item<FMT, PHASE, 8, false>(p, c, lds, mt, nt);
+      if (nb <= 1) gemm_item<FMT, PHASE, 1, false>(p, c, lds, mt, nt, reserve);
+      else if (nb <= 2) gemm_item<FMT, PHASE, 2, false>(p, c, lds, mt, nt, reserve);
+      else if (nb <= 4) gemm_item<FMT, PHASE, 4, false>(p, c, lds, mt, nt, reserve);
+      else if (nb <= 6) gemm_item<FMT, PHASE, 6, false>(p, c, lds, mt, nt, reserve);
+      else gemm_item<FMT, PHASE, 8, false>(p, c, lds, mt, nt, reserve);
     }
+    if (threadIdx.x == 0) s_item[par ^ 1] = tried < 8 ? take(ticket) : -1;
+    lds_barrier();
   }
 }
 
