@@ -330,7 +330,6 @@ __global__ __launch_bounds__(kF1Threads, 1) void decode_fc1_kernel(FusedParams p
   const int n_items = live_blocks * n_it;
   const int my_items = (n_items - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
   const int U = my_items * spw;
-  const int U2 = (U + 1) & ~1;                                // even: units are taken in pairs
 
   // Loads are unconditional so that the wait counters stay exact: units past the end and
   // K blocks past kb1 re-read a valid block (an L2 hit) whose contribution is skipped. The
@@ -458,6 +457,9 @@ __global__ __launch_bounds__(kF1Threads, 1) void decode_fc1_kernel(FusedParams p
 
   // A unit's register set is refilled right after its MFMAs, before the item's epilogue and
   // its barrier, so the weight stream keeps flowing while waves wait there.
+  // (Loading only units that exist in the last iterations, as FC2 does, made this kernel's
+  // code larger and its m = 8 time bimodal, 74.6 or 76.2 us; the re-reads stay here.)
+  const int U2 = (U + 1) & ~1;                                // even: units are taken in pairs
   for (int u = 0; u < U2; u += 2) {
     compute(u, ra);
     const int2 ia = ra.info;
@@ -653,7 +655,6 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
   int* sexp = reinterpret_cast<int*>(reinterpret_cast<uint8_t*>(sroute) + f3_table_bytes(p.cap_blocks));    // [routes] f16 exponents
   float* tacc = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(sexp) + f3_exp_bytes(routes));          // [waves][m][16 RG]
   const int U = nb > wave ? (nb - wave + kF3Waves - 1) / kF3Waves : 0;
-  const int U2 = (U + 1) & ~1;
   const int sc_lane = FMT == FMT_NVFP4 ? ((lane >> 5) * 16 + col) * 16 : col * 16;
 
   // Staging: the slot -> route table and each route's K slice by DMA (dropped routes, the
@@ -745,10 +746,8 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
   static_assert(kScaleChunkKB % kF3KB == 0 && (kF3KB == 2 || kF3KB == 4), "a workgroup's K blocks never straddle a scale chunk");
 
   F3Unit<RG> ra, rb;
-  if (U > 0) {
-    issue(0, ra);
-    issue(1, rb);
-  }
+  if (U > 0) issue(0, ra);
+  if (U > 1) issue(1, rb);
   if constexpr (W8) {
 #pragma unroll
     for (int i = 0; i < kPre; ++i) round_task(i * kF3Threads + tid, pre[i]);
@@ -858,12 +857,22 @@ __global__ __launch_bounds__(kF3Threads, 4) void decode_fc2_split_kernel(FusedPa
     }
   };
 
-  for (int u = 0; u < U2; u += 2) {
+  // The last (up to three) units issue loads only for units that exist: re-reading a unit
+  // for exact wait counts there only kept the launch waiting for loads nobody uses (m = 1:
+  // FC2 17.0 -> 15.5 us).
+  int u = 0;
+  for (; u + 3 < U; u += 2) {
     compute(u, ra);
     issue(u + 2, ra);
     compute(u + 1, rb);
     issue(u + 3, rb);
   }
+  if (u < U) {
+    compute(u, ra);
+    if (u + 2 < U) issue(u + 2, ra);
+  }
+  if (u + 1 < U) compute(u + 1, rb);
+  if (u + 2 < U) compute(u + 2, ra);
   lds_barrier();
   // Fixed-order sum over the waves: the partial of K split z for rows of this group.
   for (int i = tid; i < m * 16 * RG; i += kF3Threads) {
