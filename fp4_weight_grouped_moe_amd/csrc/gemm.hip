@@ -38,6 +38,7 @@ constexpr int kBlockBytes = kBlockM * kRowBytes;        // one route block of a 
 constexpr int kLdsBytes = 131072;                       // the activation stage ring
 constexpr int kW8AmaxOffset = 98304;                    // W4A8 FC1 epilogue: per-wave group maxima (4 KiB)
 constexpr int kEarlyTicketKB = 32;                      // items up to this many K blocks take their successor's ticket early
+constexpr int kEpilogueStage = kW8AmaxOffset + 4096;    // the epilogue's per-route values (16 B per route slot)
 
 // Wave layout and pipeline depth for tiles of NB route blocks: the 8 waves split the N tile,
 // 2 row groups x NB blocks each, so every fragment is loaded and dequantised by exactly one
@@ -170,6 +171,36 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
   const int nb = __builtin_amdgcn_readfirstlane(tile.y & 0xFF);
   const int e = __builtin_amdgcn_readfirstlane(tile.y >> 8);
   const int kbs = c.kbs;
+
+  // The epilogue's per-route values -- FC1: token, router weight and (f16 route) the token's
+  // exponent and sum of squares; FC2: route id and row exponent. Tiles of 4 or more blocks
+  // load them now (thread s for slot s of the tile) and stage them in LDS past the stage ring
+  // after the K loop, so that their epilogue waits on no global round trip (the token gathers
+  // go out once the first stage has landed, which the slot loads, issued before it, have
+  // too): prefill FC1 -1 %. Smaller tiles, whose epilogue is short, load them there (the
+  // staging barrier cost them more than it saved).
+  static_assert(kEpilogueStage + NB * kBlockM * 16 <= kLdsBytes, "epilogue staging fits in LDS");
+  const bool staged_epi = NB >= 4 && (PHASE == 1 ? !p.w4a8 : !p.atomic_bf16);
+  const bool stager = staged_epi && tid < NB * kBlockM;
+  int4 epi = make_int4(-1, 0, 0, 0);
+  if (stager) {
+    const int64_t sslot = (fb + min(tid / kBlockM, nb - 1)) * kBlockM + (tid % kBlockM);
+    if (PHASE == 1) {
+      const int2 v = p.slot_info[sslot];
+      epi.x = v.x;
+      epi.y = v.y;
+    } else {
+      epi.x = p.sorted_route_ids[sslot];
+      epi.y = F16 ? p.sexp[sslot] : 0;
+    }
+  }
+  auto gather_tokens = [&]() {
+    if (PHASE == 1 && F16 && stager) {
+      const int t = max(epi.x, 0);
+      epi.z = p.xexp[t];
+      epi.w = __float_as_int(p.xss[t]);
+    }
+  };
 
   // Activation loads. A route block's K block (16 rows x 256 B) sits in LDS as 32 half-row
   // slots of 128 B: row r = 8 r3 + r7, half h goes to slot 4 r7 + 2 h + r3, and its 16-byte
@@ -313,7 +344,10 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
   auto step = [&](int kb, int j) {
     wait_vmcnt<(D - 2) * XD>();
     stage_barrier();
-    if (kb == 0 && early_ticket) take_ticket();
+    if (kb == 0) {
+      if (early_ticket) take_ticket();
+      gather_tokens();
+    }
     __builtin_amdgcn_sched_barrier(0);
     const int jn = (j + D - 1) % D;
     compute(j, wr[j], sc[j], kb + D - 1, jn, wr[jn], sc[jn]);
@@ -332,6 +366,11 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
   // Drain the stages issued past K before the slots are reused by the next item.
   wait_vmcnt<0>();
   if (!early_ticket) take_ticket();
+  const int4* epi_lds = reinterpret_cast<const int4*>(lds + kEpilogueStage);
+  if (staged_epi) {
+    if (stager) reinterpret_cast<int4*>(lds + kEpilogueStage)[tid] = epi;
+    lds_barrier();
+  }
 
   // Epilogue. Lane (r0 = 4 (lane / 16), col = lane % 16) holds rows r0..r0+3 of each
   // 16-row group, route column col of each block.
@@ -410,20 +449,30 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
   if (PHASE == 1) {
     const float g13 = p.g13[e], g2 = p.g2[e];
     const float n_gate = F16 ? p.n13[2 * e] : 0.f, n_up = F16 ? p.n13[2 * e + 1] : 0.f;
-    // The per-route values, loaded all together first (one round trip for the slots, one for
-    // their tokens' exponents and sums of squares) from clamped addresses, so that no load is
-    // predicated and none waits behind another.
+    // The per-route values: staged in LDS above, or loaded all together here (one round trip
+    // for the slots, one for their tokens' exponents and sums of squares) from clamped
+    // addresses, so that no load is predicated and none waits behind another.
     int2 info[BW];
-#pragma unroll
-    for (int bb = 0; bb < BW; ++bb) info[bb] = p.slot_info[(fb + min(bb, nb - 1)) * kBlockM + col];
     int xe[BW];
     float xs[BW];
-    if constexpr (F16) {
+    if constexpr (NB >= 4) {
 #pragma unroll
       for (int bb = 0; bb < BW; ++bb) {
-        const int t = max(info[bb].x, 0);
-        xe[bb] = p.xexp[t];
-        xs[bb] = p.xss[t];
+        const int4 v = epi_lds[bb * kBlockM + col];
+        info[bb] = make_int2(v.x, v.y);
+        xe[bb] = v.z;
+        xs[bb] = __int_as_float(v.w);
+      }
+    } else {
+#pragma unroll
+      for (int bb = 0; bb < BW; ++bb) info[bb] = p.slot_info[(fb + min(bb, nb - 1)) * kBlockM + col];
+      if constexpr (F16) {
+#pragma unroll
+        for (int bb = 0; bb < BW; ++bb) {
+          const int t = max(info[bb].x, 0);
+          xe[bb] = p.xexp[t];
+          xs[bb] = p.xss[t];
+        }
       }
     }
 #pragma unroll
@@ -500,13 +549,19 @@ __device__ __forceinline__ void gemm_item(const FusedParams& p, const GemmCtx& c
       }
     }
   } else {
-    // (route ids and row exponents loaded together first, as in FC1's epilogue)
+    // (route ids and row exponents: staged in LDS above, or loaded together here)
     int rid[BW], qv[BW];
 #pragma unroll
     for (int bb = 0; bb < BW; ++bb) {
-      const int64_t slot = (fb + min(bb, nb - 1)) * kBlockM + col;
-      rid[bb] = p.sorted_route_ids[slot];
-      qv[bb] = F16 ? p.sexp[slot] : 0;
+      if constexpr (NB >= 4) {
+        const int4 v = epi_lds[bb * kBlockM + col];
+        rid[bb] = v.x;
+        qv[bb] = v.y;
+      } else {
+        const int64_t slot = (fb + min(bb, nb - 1)) * kBlockM + col;
+        rid[bb] = p.sorted_route_ids[slot];
+        qv[bb] = F16 ? p.sexp[slot] : 0;
+      }
     }
 #pragma unroll
     for (int bb = 0; bb < BW; ++bb) {
