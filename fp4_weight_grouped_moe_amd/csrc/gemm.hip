@@ -9,8 +9,9 @@
 // Items are (M tile, N tile) pairs: an M tile is up to 8 route blocks (128 rows) of one
 // expert, an N tile 16 row groups (256 weight rows). One 8-wave workgroup per CU, two waves
 // per SIMD, so that one wave's waits on loads and LDS reads are covered by the other's MFMAs
-// (VALU issue still takes matrix-core time on gfx950: each wave's dequantisation is kept to
-// about one VALU op per MFMA). The tile's activation K blocks stream through a ring of LDS
+// (at about one VALU op per MFMA the dequantisation hides behind the other wave's MFMAs; at
+// three per MFMA it costs a fifth of the rate; the activation reads from LDS, one per two
+// MFMAs, are what bounds the loop). The tile's activation K blocks stream through a ring of LDS
 // stages filled by buffer loads that write LDS directly; each wave streams its own two row
 // groups' E2M1 fragments and scales into a register ring of the same depth, dequantises them
 // in registers into MFMA A operands and reads activation fragments (B operands) from the stage.
@@ -20,8 +21,9 @@
 //  * FC2 epilogue: the weighted row of each route rounded to bf16; the combine pass sums each
 //    token's top-k rows in fp32 in a fixed order (deterministic, no atomics) and casts to bf16.
 //  * W4A8 FC2: the block-scaled FP4 x FP8 MFMA on FC1's MXFP8 codes (gemm_item_w8).
-// NVFP4 FC1 runs on f16 operands: activations pre-scaled per token by a power of two, E2M1 x
-// E4M3 products exact in f16 (half the dequantisation work of the bf16 route).
+// NVFP4 runs on f16 operands in both GEMMs: FC1 on activations pre-scaled per token by a power
+// of two, FC2 on intermediate rows stored as f16 times a per-slot power of two; E2M1 x E4M3
+// products are exact in f16 (half the dequantisation work of the bf16 route).
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
