@@ -361,8 +361,10 @@ def measure(layer, m, steps, warmup, args, passes):
         # The grouped GEMM is bound by whichever of its two algorithmic floors is higher: the
         # useful MFMA flops at the dense peak of its operand type, or the bytes it must move
         # (the touched experts' weights, the activation rows read and the rows written) at
-        # the HBM peak. At m = 2048 over 256 experts (~64 routes per expert) the weight bytes
-        # set the floor: about 230 flops per weight byte, under the chip's ~310 flop/byte ridge.
+        # the HBM peak. FC1 at m = 2048 over 256 experts (~64 routes per expert) does about 400
+        # flops per byte it must move, above the chip's ~310 flop/byte ridge (2.5 PFLOP/s over
+        # 8 TB/s), so the MFMA floor binds there; the few-route tiles of the edge and small
+        # shapes fall below the ridge and report the HBM floor.
         dom = "fc1" if np.mean(per["fc1"]) >= np.mean(per["fc2"]) else "fc2"
         t_dom = float(np.mean(per[dom])) * 1e-3
         if dom == "fc1":
