@@ -412,6 +412,22 @@ def test_fused_full_size_every_output(moe, device, name, ms):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.timeout(900)
+def test_fused_full_size_prefill_mxfp4_every_output(moe, device):
+    """The prefill shape (256 experts, hidden 7168, inter 2048, top-8, Zipf routing, m = 2048)
+    with MXFP4 weights on the W4A16 layer: the bf16-operand grouped GEMM (E8M0 scales folded into
+    the FP4 convert) over full 8-block tiles, 56 FC1 and 16 FC2 K blocks, 16 / 28 N tiles per M
+    tile and the per-XCD queues. Every token x every column against the oracle."""
+    case = full_case("prefill", 2048, device, fmt="mxfp4")
+    layer = make_layer(case, device)
+    _say("full prefill mxfp4 m=2048")
+    got = bf16_tensor_to_f64(run_layer(layer, case, device))
+    assert np.all(np.isfinite(got))
+    _check(case, got, label="prefill mxfp4 m=2048, every token x every column")
+    del layer, case
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("path", ["decode", "gemm"])
 def test_tiny_and_zero_activation_rows(moe, device, path):
     """A token row scaled by 1e-36 (its maximum below 2^-113, where the f16 conversion's power-of-two
