@@ -428,6 +428,33 @@ def test_fused_full_size_prefill_mxfp4_every_output(moe, device):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("act", ["relu2", "silu_swiglu"])
+@pytest.mark.parametrize("path,m", [("decode", 5), ("decode", 16), ("gemm", 40), ("gemm", 512)])
+def test_fused_every_format_and_activation(moe, device, fmt, act, path, m):
+    """Both weight formats with both activations on both paths (the workloads pair MXFP4 only
+    with SiLU-SwiGLU and relu2 only with NVFP4, whose intermediate rows the two formats store
+    differently: bf16 for MXFP4, f16 times a per-slot power of two for NVFP4 on the grouped
+    GEMM). Intermediate 400 (a partial 32-group for MXFP4, a 128-block tail for both), an
+    expert map with dropped ids; m = 512 puts ~100 routes on each of the 8 local experts (full
+    8-block tiles). Every output against the oracle, and a second call equal to the first."""
+    import dataclasses
+    cfg = dataclasses.replace(C.get_config("edge"), num_experts=8, num_global_experts=16, hidden=512, inter=400,
+                              act=act, fmt=fmt, name=f"edge_{fmt}_{act}")
+    _say(f"{fmt} {act} m={m} path={path}")
+    case = make_case(cfg, m, seed=m * 7 + len(act) + len(fmt), weights="normal")
+    layer = make_layer(case, device)
+    moe.moe_w4a16_set_path(path)
+    try:
+        got = bf16_tensor_to_f64(run_layer(layer, case, device))
+        again = bf16_tensor_to_f64(run_layer(layer, case, device))
+    finally:
+        moe.moe_w4a16_set_path("auto")
+    assert np.array_equal(got, again)
+    assert np.all(np.isfinite(got))
+    _check(case, got, label=f"{fmt} {act} m={m} {path}")
+
+
 @pytest.mark.parametrize("path", ["decode", "gemm"])
 def test_tiny_and_zero_activation_rows(moe, device, path):
     """A token row scaled by 1e-36 (its maximum below 2^-113, where the f16 conversion's power-of-two
