@@ -371,11 +371,15 @@ def test_decode_path_map_and_dropped_routes(moe, device, name, m):
 # ----------------------------------------------------------------------------- full-size, every output
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name,m", [("decode", 12), ("decode", 16), ("small", 16), ("edge", 16)])
+@pytest.mark.parametrize("name,m", [("decode", 12), ("decode", 16), ("small", 16), ("edge", 16), ("prefill", 4),
+                                    ("prefill", 12), ("prefill", 16)])
 def test_decode_path_full_size_above_eight_tokens(moe, device, name, m):
     """The decode path at 9..16 tokens stages more than 64 KiB of activation rows (one FC1
     workgroup per CU, routes packed by the route-pack launch; the edge shape adds an expert
-    map and -1 ids): every output of the full-size layer against the oracle."""
+    map and -1 ids); on the prefill shape (hidden 7168) beyond 9 tokens the rows exceed the
+    128 KiB of LDS and FC1 reads them from memory, NVFP4 on the bf16 route, and at 4 tokens
+    the FC1 launch packs the routes itself over 256 experts: every output of the full-size
+    layer against the oracle."""
     case = full_case(name, m, device)
     layer = make_layer(case, device, token_capacity=RP.token_capacity(m))
     _say(f"full {name} m={m} path=decode")
