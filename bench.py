@@ -129,6 +129,23 @@ def expert_bytes(cfg):
     return w13, w2
 
 
+# The arithmetic the layer's contractions run in (inputs and outputs are bf16 throughout).
+DTYPE_NOTES = {
+    "f16": "NVFP4 weights: f16 MFMA operands (E2M1 x E4M3 exact in f16; activations times a per-token "
+           "power of two, exact above 2^-38 of the row maximum; grouped-GEMM intermediate rows f16 times a "
+           "per-slot power of two), fp32 accumulation",
+    "bf16": "MXFP4 weights: bf16 MFMA operands (E2M1 x E8M0 exact in bf16), fp32 accumulation",
+    "bf16+fp8": "W4A8: FC1 on bf16 operands; FC2 on the block-scaled FP4 x FP8 MFMA (activation output rounded "
+                "to MXFP8); fp32 accumulation",
+}
+
+
+def compute_dtype(cfg, args):
+    if args.w4a8:
+        return "bf16+fp8"
+    return "f16" if cfg.fmt == "nvfp4" else "bf16"
+
+
 def source_digest(*names):
     h = hashlib.sha256()
     for n in names:
@@ -439,7 +456,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": compute_dtype(cfg, args),
+        "dtype_note": DTYPE_NOTES[compute_dtype(cfg, args)],
         "data": "synthetic",
         "config": {"workload": head["workload"], "m": m, "token_capacity": head["token_capacity"],
                    "routing_sets": head["routing_sets"], "path": head["path"], "timing": key,
